@@ -1,0 +1,23 @@
+// Host-side helpers shared by the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp8bs.h"
+
+namespace fp8bs {
+
+// Largest 1-D grid the launchers use (gridDim.x is 32 bits; keep well inside it).
+constexpr int64_t kMaxGrid = 0x7FFFFFFFLL;
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Status after enqueueing: a launch the runtime rejected is reported here; a
+// fault inside a kernel surfaces at the caller's next synchronization.
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH;
+}
+
+}  // namespace fp8bs

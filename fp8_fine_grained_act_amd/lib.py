@@ -1,0 +1,205 @@
+"""ctypes binding of libfp8bs.so with the C names, taking torch tensors.
+
+The binding only marshals arguments: it checks dtypes, devices and strides,
+allocates outputs with torch (device memory is torch's job here) and passes raw
+pointers plus the current HIP stream to the library.  Every step of the
+computation runs in the library's HIP kernels.  There is no fallback: when the
+library is missing the import fails, and a non-zero status raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
+
+FP8BS_OK = 0
+GROUP = 128
+
+_c_void_p, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+
+_SIGNATURES = {
+    "fp8bs_quantize_act_1x128": [_c_void_p, _i64, _i64, _i64, _int, _c_void_p, _i64, _c_void_p, _c_void_p],
+    "fp8bs_quantize_w_128x128": [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p],
+    "fp8bs_gemm": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int, _c_void_p, _i64,
+                   _c_void_p],
+    "fp8bs_grouped_gemm": [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64, _i64,
+                           _c_void_p, _c_void_p],
+    "fp8bs_gemm_wgrad": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _int,
+                         _c_void_p],
+}
+
+
+class Fp8bsError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: {status_string(status)}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m fp8_fine_grained_act_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.fp8bs_status_string.argtypes = [ctypes.c_int]
+    lib.fp8bs_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+raw = _load()
+EXPORTED = tuple(_SIGNATURES) + ("fp8bs_status_string",)
+
+
+def status_string(status):
+    return raw.fp8bs_status_string(int(status)).decode()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, status):
+    if status != FP8BS_OK:
+        raise Fp8bsError(fn, status)
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA/HIP tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    return t
+
+
+def _row_major(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def fp8bs_quantize_act_1x128(x, transpose=0, q=None, scales=None, stream=None):
+    """1x128 tile quantization of bf16 x [rows, cols].
+
+    transpose=0: q uint8 [rows, cols], scales f32 [rows, cols/128].
+    transpose=1: q uint8 [cols, rows], scales f32 [cols, rows/128] (tiles along rows).
+    """
+    _dev(x, torch.bfloat16, "x")
+    ldx = _row_major(x, "x")
+    rows, cols = x.shape
+    if transpose:
+        qshape, sshape = (cols, rows), (cols, rows // GROUP)
+    else:
+        qshape, sshape = (rows, cols), (rows, cols // GROUP)
+    if q is None:
+        q = torch.empty(qshape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    _dev(q, torch.uint8, "q")
+    _dev(scales, torch.float32, "scales")
+    ldq = _row_major(q, "q")
+    if tuple(q.shape) != qshape or tuple(scales.shape) != sshape or not scales.is_contiguous():
+        raise ValueError("output shapes do not match the input")
+    st = raw.fp8bs_quantize_act_1x128(x.data_ptr(), rows, cols, ldx, int(bool(transpose)), q.data_ptr(), ldq,
+                                      scales.data_ptr(), _stream(stream))
+    _check("fp8bs_quantize_act_1x128", st)
+    return q, scales
+
+
+def fp8bs_quantize_w_128x128(w, q=None, scales=None, stream=None):
+    """128x128 block quantization of bf16 w [n, k] (or [E, N, K], viewed as [E*N, K])."""
+    _dev(w, torch.bfloat16, "w")
+    lead = tuple(w.shape[:-2])
+    w2 = w.reshape(-1, w.shape[-1]) if w.dim() == 3 else w
+    ldw = _row_major(w2, "w")
+    n, k = w2.shape
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(lead + (w.shape[-2] // GROUP, k // GROUP), dtype=torch.float32, device=w.device)
+    _dev(q, torch.uint8, "q")
+    q2 = q.reshape(-1, q.shape[-1]) if q.dim() == 3 else q
+    ldq = _row_major(q2, "q")
+    if tuple(q2.shape) != (n, k) or scales.numel() != (n // GROUP) * (k // GROUP) or not scales.is_contiguous():
+        raise ValueError("output shapes do not match the input")
+    st = raw.fp8bs_quantize_w_128x128(w2.data_ptr(), n, k, ldw, q2.data_ptr(), ldq, scales.data_ptr(),
+                                      _stream(stream))
+    _check("fp8bs_quantize_w_128x128", st)
+    return q, scales
+
+
+def fp8bs_gemm(qa, sa, qb, sb, b_layout=0, c=None, stream=None):
+    """bf16 C [m, n] from E4M3 A [m, k] and B ([n, k] for b_layout 0, [k, n] for 1)."""
+    for t, nm in ((qa, "qa"), (qb, "qb")):
+        _dev(t, torch.uint8, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    for t, nm in ((sa, "sa"), (sb, "sb")):
+        _dev(t, torch.float32, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    m, k = qa.shape
+    n = qb.shape[0] if b_layout == 0 else qb.shape[1]
+    if c is None:
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=qa.device)
+    _dev(c, torch.bfloat16, "c")
+    ldc = _row_major(c, "c")
+    st = raw.fp8bs_gemm(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(), m, n, k, int(b_layout),
+                        c.data_ptr(), ldc, _stream(stream))
+    _check("fp8bs_gemm", st)
+    return c
+
+
+def fp8bs_grouped_gemm(qa, sa, seg_offsets, qb, sb, c=None, stream=None):
+    """MoE grouped GEMM: bf16 C [R, n]; qb [E, n, k]; seg_offsets int32 [E+1] on the device."""
+    _dev(qa, torch.uint8, "qa")
+    _dev(qb, torch.uint8, "qb")
+    _dev(sa, torch.float32, "sa")
+    _dev(sb, torch.float32, "sb")
+    _dev(seg_offsets, torch.int32, "seg_offsets")
+    for t, nm in ((qa, "qa"), (qb, "qb"), (sa, "sa"), (sb, "sb"), (seg_offsets, "seg_offsets")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    rows, k = qa.shape
+    num_e, n = qb.shape[0], qb.shape[1]
+    if seg_offsets.numel() != num_e + 1:
+        raise ValueError("seg_offsets must have num_experts + 1 entries")
+    if c is None:
+        c = torch.empty((rows, n), dtype=torch.bfloat16, device=qa.device)
+    _dev(c, torch.bfloat16, "c")
+    if not c.is_contiguous():
+        raise ValueError("c must be contiguous")
+    st = raw.fp8bs_grouped_gemm(qa.data_ptr(), sa.data_ptr(), seg_offsets.data_ptr(), num_e, rows, qb.data_ptr(),
+                                sb.data_ptr(), n, k, c.data_ptr(), _stream(stream))
+    _check("fp8bs_grouped_gemm", st)
+    return c
+
+
+def fp8bs_gemm_wgrad(qa, sa, qb, sb, c=None, accumulate=0, stream=None):
+    """f32 C [m, n] (+)= A B^T over tokens; A [m, t], B [n, t], per-row scales [*, t/128]."""
+    for t, nm in ((qa, "qa"), (qb, "qb")):
+        _dev(t, torch.uint8, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    for t, nm in ((sa, "sa"), (sb, "sb")):
+        _dev(t, torch.float32, nm)
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    m, t_len = qa.shape
+    n = qb.shape[0]
+    if c is None:
+        c = torch.empty((m, n), dtype=torch.float32, device=qa.device)
+    _dev(c, torch.float32, "c")
+    ldc = _row_major(c, "c")
+    st = raw.fp8bs_gemm_wgrad(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(), m, n, t_len,
+                              c.data_ptr(), ldc, int(accumulate), _stream(stream))
+    _check("fp8bs_gemm_wgrad", st)
+    return c

@@ -1,0 +1,153 @@
+/*
+ * fp8bs -- block-scaled FP8 quantization and GEMMs for AMD MI355X (gfx950).
+ *
+ * C ABI of the library libfp8bs.so.  Every entry point takes plain device
+ * pointers and sizes, enqueues its kernels on the caller's HIP stream and
+ * returns at once; nothing is allocated, and the library keeps no state, so
+ * calls are re-entrant and thread-safe.  The caller owns every buffer.
+ *
+ * The method (pages cited by title and section):
+ *   "DeepSeek-V3 技术报告深度解读" (sherconan.github.io), section 3 "FP8 混合精度训练":
+ *     all three GEMMs of a linear layer (forward, activation gradient, weight
+ *     gradient) take FP8 inputs; activations are scaled per 1x128 tile and
+ *     weights per 128x128 block; partial sums are promoted to FP32 after each
+ *     128-element stretch of the contraction.
+ *   deepseek.csdn.net page, section 二(四) "FP8 低精度训练", and the qqstock.cn
+ *   page, section "FP8 低精度訓練：精度與效率的平衡": the same tile/block
+ *   granularity in place of per-tensor scaling, FP32 accumulation of the
+ *   matrix-multiply partials, routed MoE experts among the FP8 GEMMs.
+ *
+ * Readings where the pages are silent (fixed here, tested against a CPU
+ * reference):
+ *   - FP8 format: OCP E4M3 "fn" (max 448, NaN only at S.1111.111, no Inf).
+ *   - Scale of a group: s = amax / 448 in IEEE binary32 (a dequantization
+ *     multiplier, not rounded to a power of two).  Code of x: E4M3
+ *     round-to-nearest-even of the binary32 quotient x / s, saturating at
+ *     +-448, sign kept also for zeros.  A group with amax == 0 gets s = 0 and
+ *     signed-zero codes.  No flush-to-zero anywhere.
+ *   - Every 128-element scale group lies along the contraction of the GEMM
+ *     that consumes it, so each 128-long partial is multiplied by one
+ *     activation scale and one weight scale and added into an FP32
+ *     accumulator: C = sum_kb sa(m,kb) * sb(n,kb) * P_kb.
+ *   - Layouts are row-major.  bf16 travels as raw uint16_t bits, E4M3 as raw
+ *     uint8_t codes, scales as float.
+ *
+ * Inputs must be finite.  Non-finite inputs give unspecified codes and results.
+ *
+ * Status codes: 0 on success; negative values are argument errors detected on
+ * the host before any kernel is enqueued (nothing has been written), or a
+ * launch error reported by the HIP runtime right after enqueueing.  Faults of
+ * enqueued kernels surface at the caller's next synchronization.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BS_OK 0
+#define FP8BS_ERR_NULL (-1)   /* a required pointer is NULL                          */
+#define FP8BS_ERR_SHAPE (-2)  /* a size is <= 0, not a required multiple, or too big  */
+#define FP8BS_ERR_ALIGN (-3)  /* a pointer or leading dimension is misaligned         */
+#define FP8BS_ERR_FLAG (-4)   /* an enum-like flag has an unknown value               */
+#define FP8BS_ERR_LAUNCH (-5) /* the HIP runtime rejected a kernel launch             */
+
+/*
+ * Activation quantization in 1x128 tiles (the pages' activation granularity).
+ *
+ * transpose == 0: tiles run along the columns.
+ *   x       bf16 [rows, cols], row stride ldx elements
+ *   q       E4M3 [rows, cols], row stride ldq bytes
+ *   scales  f32  [rows, cols/128], row-major, contiguous
+ *   cols % 128 == 0, rows >= 1 (any value).
+ * transpose == 1: tiles run along the rows (128 consecutive rows of one
+ *   column), the output is the transposed matrix.  This feeds the weight
+ *   gradient, whose contraction runs over tokens (the rows of x).
+ *   x       bf16 [rows, cols], row stride ldx elements
+ *   q       E4M3 [cols, rows], row stride ldq bytes
+ *   scales  f32  [cols, rows/128], row-major, contiguous
+ *   rows % 128 == 0, cols >= 1 with cols % 8 == 0.
+ *   The result equals transpose == 0 applied to x^T.
+ * Alignment: x and q 16-byte aligned, ldx % 8 == 0, ldq % 16 == 0, scales
+ * 4-byte aligned; ldx >= cols and ldq >= the output row length.
+ */
+int fp8bs_quantize_act_1x128(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             int transpose, uint8_t* q, int64_t ldq, float* scales,
+                             void* stream);
+
+/*
+ * Weight quantization in 128x128 blocks (the pages' weight granularity).
+ *   w       bf16 [n, k], row stride ldw elements
+ *   q       E4M3 [n, k], row stride ldq bytes
+ *   scales  f32  [n/128, k/128], row-major, contiguous
+ *   n % 128 == 0, k % 128 == 0.  Stacked expert weights [E, N, K] are passed
+ *   as n = E * N (blocks never straddle experts because N % 128 == 0).
+ * Alignment: w and q 16-byte aligned, ldw % 8 == 0, ldq % 16 == 0.
+ */
+int fp8bs_quantize_w_128x128(const uint16_t* w, int64_t n, int64_t k, int64_t ldw,
+                             uint8_t* q, int64_t ldq, float* scales, void* stream);
+
+/*
+ * Block-scaled GEMM with bf16 output: C[m, n] = sum_k A[m, k] * B(k, n), the
+ * contraction in 128-long blocks, each block's FP32 partial multiplied by
+ * sa[m, kb] * sb(kb, n-block) and added to an FP32 accumulator; the result is
+ * rounded to bf16 (nearest, ties to even).
+ *   qa  E4M3 [m, k] contiguous,  sa f32 [m, k/128] contiguous (1x128 tiles)
+ *   b_layout == 0 (forward, y = x W^T):
+ *       qb E4M3 [n, k] contiguous, sb f32 [n/128, k/128] (128x128 blocks)
+ *   b_layout == 1 (activation gradient, dx = dy W, with the forward weight
+ *       used as stored): qb E4M3 [k, n] contiguous, sb f32 [k/128, n/128]
+ *   c   bf16 [m, n], row stride ldc elements
+ *   m >= 1 (any), n % 128 == 0, k % 128 == 0.
+ * Alignment: qa, qb, c 16-byte aligned; ldc % 8 == 0, ldc >= n.
+ */
+int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
+               int64_t m, int64_t n, int64_t k, int b_layout, uint16_t* c, int64_t ldc,
+               void* stream);
+
+/*
+ * MoE grouped GEMM (forward) over expert row segments.  The rows of expert e
+ * are [seg_offsets[e], seg_offsets[e+1]); each segment gets fp8bs_gemm
+ * (b_layout 0) with that expert's weight.
+ *   qa          E4M3 [total_rows, k], sa f32 [total_rows, k/128]
+ *   seg_offsets int32 [num_experts + 1], DEVICE memory
+ *   qb          E4M3 [num_experts, n, k], sb f32 [num_experts, n/128, k/128]
+ *   c           bf16 [total_rows, n] contiguous
+ *   total_rows % 128 == 0, n % 128 == 0, k % 128 == 0, 1 <= num_experts <= 65536.
+ * Preconditions on seg_offsets (not checked: they live on the device):
+ * seg_offsets[0] == 0, non-decreasing, every entry a multiple of 128,
+ * seg_offsets[num_experts] == total_rows.  Empty segments are allowed.
+ * Padding rows (rows of a segment beyond the expert's routed rows) are
+ * expected to hold zeros in the bf16 source, so their codes and scales are
+ * zero and their outputs are exactly 0.
+ */
+int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int32_t* seg_offsets,
+                       int64_t num_experts, int64_t total_rows, const uint8_t* qb,
+                       const float* sb, int64_t n, int64_t k, uint16_t* c, void* stream);
+
+/*
+ * Weight-gradient GEMM: C[m, n] (+)= sum_t A[m, t] * B[n, t] over tokens t,
+ * with per-row scales on both operands (both come from
+ * fp8bs_quantize_act_1x128 with transpose == 1), FP32 output.
+ *   qa  E4M3 [m, t] contiguous, sa f32 [m, t/128]
+ *   qb  E4M3 [n, t] contiguous, sb f32 [n, t/128]
+ *   c   f32 [m, n], row stride ldc elements
+ *   accumulate == 0 overwrites c, == 1 adds to it (gradient accumulation).
+ *   t % 128 == 0, m >= 1, n >= 1 with n % 4 == 0.
+ * Alignment: qa, qb, c 16-byte aligned; ldc % 4 == 0, ldc >= n.
+ */
+int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
+                     int64_t m, int64_t n, int64_t t, float* c, int64_t ldc, int accumulate,
+                     void* stream);
+
+/* Short English text for a status code (static storage, never NULL). */
+const char* fp8bs_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host with the documented status codes (no kernel is launched
+on any of these paths, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+OK, ENULL, ESHAPE, EALIGN, EFLAG = 0, -1, -2, -3, -4
+P = 0x100000          # a 16-byte aligned stand-in pointer, never dereferenced on these paths
+P_ODD = P + 4
+
+
+@pytest.fixture(scope="module")
+def raw():
+    from fp8_fine_grained_act_amd import lib
+
+    return lib.raw
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"\b(fp8bs_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("fp8bs_quantize_act_1x128", "fp8bs_quantize_w_128x128", "fp8bs_gemm", "fp8bs_grouped_gemm",
+              "fp8bs_gemm_wgrad", "fp8bs_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(raw):
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+        assert isinstance(getattr(raw, name), ctypes._CFuncPtr)
+
+
+def test_status_strings(raw):
+    from fp8_fine_grained_act_amd import lib
+
+    assert lib.status_string(OK) == "ok"
+    for s in (ENULL, ESHAPE, EALIGN, EFLAG, -5):
+        assert lib.status_string(s) not in ("ok", "unknown status")
+    assert lib.status_string(123) == "unknown status"
+
+
+def test_quantize_act_validation(raw):
+    f = raw.fp8bs_quantize_act_1x128
+    assert f(None, 4, 128, 128, 0, P, 128, P, None) == ENULL
+    assert f(P, 4, 128, 128, 2, P, 128, P, None) == EFLAG
+    assert f(P, 4, 100, 128, 0, P, 128, P, None) == ESHAPE          # cols % 128
+    assert f(P, 0, 128, 128, 0, P, 128, P, None) == ESHAPE
+    assert f(P, 4, 128, 64, 0, P, 128, P, None) == ESHAPE           # ldx < cols
+    assert f(P_ODD, 4, 128, 128, 0, P, 128, P, None) == EALIGN
+    assert f(P, 4, 128, 130, 0, P, 128, P, None) == EALIGN          # ldx % 8
+    assert f(P, 4, 128, 128, 0, P, 136, P, None) == EALIGN          # ldq % 16
+    assert f(P, 100, 64, 64, 1, P, 112, P, None) == ESHAPE          # transposed: rows % 128
+    assert f(P, 128, 60, 64, 1, P, 128, P, None) == ESHAPE          # transposed: cols % 8
+    assert f(P, 128, 64, 64, 1, P, 64, P, None) == ESHAPE           # transposed: ldq < rows
+
+
+def test_quantize_w_validation(raw):
+    f = raw.fp8bs_quantize_w_128x128
+    assert f(P, 128, 128, 128, None, 128, P, None) == ENULL
+    assert f(P, 100, 128, 128, P, 128, P, None) == ESHAPE
+    assert f(P, 128, 200, 200, P, 208, P, None) == ESHAPE
+    assert f(P, 128, 128, 128, P_ODD, 128, P, None) == EALIGN
+
+
+def test_gemm_validation(raw):
+    f = raw.fp8bs_gemm
+    assert f(P, P, P, None, 4, 128, 128, 0, P, 128, None) == ENULL
+    assert f(P, P, P, P, 4, 128, 128, 3, P, 128, None) == EFLAG
+    assert f(P, P, P, P, 4, 100, 128, 0, P, 128, None) == ESHAPE    # n % 128
+    assert f(P, P, P, P, 4, 128, 100, 0, P, 128, None) == ESHAPE    # k % 128
+    assert f(P, P, P, P, 0, 128, 128, 0, P, 128, None) == ESHAPE
+    assert f(P, P, P, P, 4, 128, 128, 0, P, 64, None) == ESHAPE     # ldc < n
+    assert f(P, P, P_ODD, P, 4, 128, 128, 0, P, 128, None) == EALIGN
+    assert f(P, P, P, P, 4, 128, 128, 0, P, 132, None) == EALIGN    # ldc % 8
+
+
+def test_grouped_validation(raw):
+    f = raw.fp8bs_grouped_gemm
+    assert f(P, P, None, 4, 512, P, P, 128, 128, P, None) == ENULL
+    assert f(P, P, P, 0, 512, P, P, 128, 128, P, None) == ESHAPE
+    assert f(P, P, P, 4, 500, P, P, 128, 128, P, None) == ESHAPE    # total_rows % 128
+    assert f(P, P, P, 4, 512, P, P, 128, 100, P, None) == ESHAPE
+    assert f(P, P, P + 2, 4, 512, P, P, 128, 128, P, None) == EALIGN
+
+
+def test_wgrad_validation(raw):
+    f = raw.fp8bs_gemm_wgrad
+    assert f(P, P, P, P, 8, 8, 128, None, 8, 0, None) == ENULL
+    assert f(P, P, P, P, 8, 8, 128, P, 8, 2, None) == EFLAG
+    assert f(P, P, P, P, 8, 8, 100, P, 8, 0, None) == ESHAPE         # t % 128
+    assert f(P, P, P, P, 8, 6, 128, P, 8, 0, None) == ESHAPE         # n % 4
+    assert f(P, P, P, P, 8, 8, 128, P, 4, 0, None) == ESHAPE         # ldc < n
+    assert f(P, P, P, P, 8, 8, 128, P, 10, 0, None) == EALIGN        # ldc % 4
+
+
+def test_binding_has_the_c_names():
+    from fp8_fine_grained_act_amd import lib
+
+    for name in declared_functions():
+        if name != "fp8bs_status_string":
+            assert callable(getattr(lib, name)), name
