@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 GEMM path on one MI355X.
+
+Default workload (one "step" = one FP8 training pass of the MLA query
+down-projection layer, X [4096, 7168] -> Y [4096, 1536], all quantization
+included; this runs every step of the hot path except the MoE grouped GEMM):
+    quantize X (1x128 tiles)             quantize W (128x128 blocks)
+    Y  = X W^T   (forward GEMM, bf16)    quantize dY (1x128 tiles)
+    dX = dY W    (dgrad GEMM, bf16)      quantize dY^T, X^T (tiles along tokens)
+    dW = dY^T X  (wgrad GEMM, f32)
+``value`` = the step's GEMM FLOPs (3 x 2*4096*1536*7168) / step time, in TFLOP/s.
+Other configurations (``--config c3|c4|c5``) print their own line.
+
+Inputs are resident in HBM before timing; the step rotates over several input
+copies (>= 256 MB in total) so the 256 MB Infinity Cache cannot hold them
+between steps.  Per-kernel durations come from HIP events recorded on the
+launch stream around every call of every timed step.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-scaled FP8 GEMM TFLOP/s and % of MI355X FP8 dense MFMA peak (1 GPU)"
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "gemm": ["fp8_fine_grained_act_amd/csrc/gemm.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
+    "quant": ["fp8_fine_grained_act_amd/csrc/quantize.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
+}
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"])
+    p.add_argument("--rotate", type=int, default=0, help="input copies to rotate over (0 = automatic)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=2048)
+    return p.parse_args()
+
+
+def source_hash(kind):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def dev_bf16(bits):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Call:
+    def __init__(self, name, kind, fn, flops=0.0, nbytes=0.0):
+        self.name, self.kind, self.fn, self.flops, self.nbytes = name, kind, fn, flops, nbytes
+        self.times_ms = []
+
+
+def build_layer_step(lib, cfg_name, rotate):
+    """Calls of one training pass of a linear layer (configs c2 / c3 shapes)."""
+    import torch
+
+    from workloads import config_by_name, layer_inputs
+
+    cfg = config_by_name(cfg_name)
+    m, n, k = cfg["M"], cfg["N"], cfg["K"]
+    d = layer_inputs(cfg)
+    x0, w0, dy0 = dev_bf16(d["a"]), dev_bf16(d["b"]), dev_bf16(d["dy"])
+    per_set = (x0.numel() + w0.numel() + dy0.numel()) * 2
+    if rotate <= 0:
+        rotate = max(2, -(-512 * 2 ** 20 // per_set))
+    sets = [(x0, w0, dy0)] + [(x0.clone(), w0.clone(), dy0.clone()) for _ in range(rotate - 1)]
+    u8, f32, bf16 = torch.uint8, torch.float32, torch.bfloat16
+    e = lambda *s, dt: torch.empty(s, dtype=dt, device="cuda")  # noqa: E731
+    qx, sx = e(m, k, dt=u8), e(m, k // 128, dt=f32)
+    qw, sw = e(n, k, dt=u8), e(n // 128, k // 128, dt=f32)
+    y = e(m, n, dt=bf16)
+    qdy, sdy = e(m, n, dt=u8), e(m, n // 128, dt=f32)
+    dx = e(m, k, dt=bf16)
+    qdyt, sdyt = e(n, m, dt=u8), e(n, m // 128, dt=f32)
+    qxt, sxt = e(k, m, dt=u8), e(k, m // 128, dt=f32)
+    dw = e(n, k, dt=f32)
+    state = {"i": 0}
+
+    def cur():
+        return sets[state["i"] % rotate]
+
+    act_bytes = lambda r, c: r * c * 3 + r * c // 128 * 4  # noqa: E731
+    calls = [
+        Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(cur()[0], q=qx, scales=sx),
+             nbytes=act_bytes(m, k)),
+        Call("quant_w", "quant", lambda: lib.fp8bs_quantize_w_128x128(cur()[1], q=qw, scales=sw),
+             nbytes=n * k * 3 + (n // 128) * (k // 128) * 4),
+        Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k),
+        Call("quant_act_dy", "quant", lambda: lib.fp8bs_quantize_act_1x128(cur()[2], q=qdy, scales=sdy),
+             nbytes=act_bytes(m, n)),
+        Call("gemm_dgrad", "gemm", lambda: lib.fp8bs_gemm(qdy, sdy, qw, sw, b_layout=1, c=dx),
+             flops=2.0 * m * n * k),
+        Call("quant_act_dy_t", "quant",
+             lambda: lib.fp8bs_quantize_act_1x128(cur()[2], transpose=1, q=qdyt, scales=sdyt),
+             nbytes=act_bytes(m, n)),
+        Call("quant_act_x_t", "quant",
+             lambda: lib.fp8bs_quantize_act_1x128(cur()[0], transpose=1, q=qxt, scales=sxt),
+             nbytes=act_bytes(m, k)),
+        Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdyt, sdyt, qxt, sxt, c=dw),
+             flops=2.0 * m * n * k),
+    ]
+    desc = dict(workload=f"{cfg_name}: one FP8 training pass (forward + dgrad + wgrad, all quantization "
+                         f"included) of a linear layer, {cfg['desc']}",
+                M_tokens=m, N_out=n, K_in=k, input_copies=rotate)
+    return calls, state, desc, d
+
+
+def build_grouped_step(lib, rotate):
+    import numpy as np
+    import torch
+
+    from workloads import config_by_name, device_expert_weights, grouped_inputs_host
+
+    cfg = config_by_name("c4")
+    g = grouped_inputs_host(cfg, with_weights=False)
+    off, counts = g["offsets"], g["counts"]
+    rows, k, n, num_e = int(off[-1]), cfg["K"], cfg["N"], cfg["experts"]
+    x = dev_bf16(g["x"])
+    w = device_expert_weights(cfg)
+    seg = torch.from_numpy(off.astype(np.int32)).cuda()
+    qx, sx = torch.empty((rows, k), dtype=torch.uint8, device="cuda"), torch.empty(
+        (rows, k // 128), dtype=torch.float32, device="cuda")
+    qw, sw = torch.empty((num_e, n, k), dtype=torch.uint8, device="cuda"), torch.empty(
+        (num_e, n // 128, k // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
+    state = {"i": 0}
+    real = float(counts.sum())
+    calls = [
+        Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, q=qx, scales=sx),
+             nbytes=rows * k * 3 + rows * k // 128 * 4),
+        Call("quant_w_experts", "quant", lambda: lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw),
+             nbytes=num_e * n * k * 3 + num_e * (n // 128) * (k // 128) * 4),
+        Call("gemm_grouped", "gemm", lambda: lib.fp8bs_grouped_gemm(qx, sx, seg, qw, sw, c=y),
+             flops=2.0 * real * n * k),
+    ]
+    desc = dict(workload="c4: MoE routed-expert forward, 4096 tokens x top-8 of 256 experts (Zipf 1.1), "
+                         "fused gate+up N=4096, K=7168; quantize X and all expert weights, grouped GEMM",
+                routed_rows=int(real), padded_rows=rows, experts=num_e, N=n, K=k,
+                gemm_flops_counted="real routed rows only")
+    return calls, state, desc, None
+
+
+def build_wgrad_step(lib, rotate):
+    import torch
+
+    from workloads import config_by_name, wgrad_inputs
+
+    cfg = config_by_name("c5")
+    t, m, n = cfg["T"], cfg["M"], cfg["N"]
+    d = wgrad_inputs(cfg)
+    dy, x = dev_bf16(d["dy"]), dev_bf16(d["x"])
+    qdy, sdy = torch.empty((m, t), dtype=torch.uint8, device="cuda"), torch.empty(
+        (m, t // 128), dtype=torch.float32, device="cuda")
+    qx, sx = torch.empty((n, t), dtype=torch.uint8, device="cuda"), torch.empty(
+        (n, t // 128), dtype=torch.float32, device="cuda")
+    dw = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    state = {"i": 0}
+    calls = [
+        Call("quant_act_dy_t", "quant", lambda: lib.fp8bs_quantize_act_1x128(dy, transpose=1, q=qdy, scales=sdy),
+             nbytes=t * m * 3 + t * m // 128 * 4),
+        Call("quant_act_x_t", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, transpose=1, q=qx, scales=sx),
+             nbytes=t * n * 3 + t * n // 128 * 4),
+        Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdy, sdy, qx, sx, c=dw), flops=2.0 * m * n * t),
+    ]
+    desc = dict(workload="c5: weight gradient dW[1536,7168] = dY^T X over 16384 tokens, both operands "
+                         "transpose-quantized along tokens", T=t, M=m, N=n)
+    return calls, state, desc, None
+
+
+def run_steps(calls, state, steps, record):
+    import torch
+
+    evs = []
+    for _ in range(steps):
+        row = []
+        for c in calls:
+            if record:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                c.fn()
+                b.record()
+                row.append((a, b))
+            else:
+                c.fn()
+        state["i"] += 1
+        evs.append(row)
+    return evs
+
+
+def cpu_baseline(cfg_name, data, sample_rows):
+    """The oracle, as it stands, on a bounded sample of the same workload (host cores)."""
+    import numpy as np
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    from oracle import (gemm_dgrad, gemm_fprop, gemm_wgrad, quantize_act_1x128, quantize_act_1x128_t,
+                        quantize_w_128x128)
+
+    x, w, dy = data["a"][:sample_rows], data["b"], data["dy"][:sample_rows]
+    m, k = x.shape
+    n = w.shape[0]
+    t0 = time.perf_counter()
+    qx, sx = quantize_act_1x128(x)
+    qw, sw = quantize_w_128x128(w)
+    gemm_fprop(qx, sx, qw, sw)
+    qdy, sdy = quantize_act_1x128(dy)
+    gemm_dgrad(qdy, sdy, qw, sw)
+    qdyt, sdyt = quantize_act_1x128_t(dy)
+    qxt, sxt = quantize_act_1x128_t(x)
+    gemm_wgrad(qdyt, sdyt, qxt, sxt)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * m * n * k
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{cfg_name} training pass restricted to the first {m} of {data['a'].shape[0]} tokens "
+                      f"(full weight [{n},{k}] quantized, forward/dgrad/wgrad GEMMs over the sampled tokens); "
+                      f"value = sampled GEMM FLOPs / oracle wall time"}
+
+
+def load_traffic(name, kind):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE, encoding="utf-8") as f:
+        tab = json.load(f)
+    ent = tab.get(name)
+    if not ent or ent.get("source_sha") != source_hash(kind):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding of the path is described in the design notes, not run.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from fp8_fine_grained_act_amd import lib
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.config in ("c2", "c3"):
+        calls, state, desc, data = build_layer_step(lib, args.config, args.rotate)
+    elif args.config == "c4":
+        calls, state, desc, data = build_grouped_step(lib, args.rotate)
+    else:
+        calls, state, desc, data = build_wgrad_step(lib, args.rotate)
+    torch.cuda.synchronize()
+
+    run_steps(calls, state, args.warmup, record=False)
+    torch.cuda.synchronize()
+
+    # timed region: steps back to back, events around every call
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs = run_steps(calls, state, args.steps, record=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for row in evs:
+        for c, (a, b) in zip(calls, row):
+            c.times_ms.append(a.elapsed_time(b))
+
+    ms_per_step = wall * 1e3 / args.steps
+    gemm_flops = sum(c.flops for c in calls)
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {}
+    for c in calls:
+        avg = sum(c.times_ms) / len(c.times_ms)
+        ent = {"avg_us": round(avg * 1e3, 2)}
+        if c.kind == "gemm":
+            tf = c.flops / (avg * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4))
+        else:
+            gb = c.nbytes / (avg * 1e-3) / 1e9
+            ent.update(gbps=round(gb, 1), frac_hbm_peak=round(gb / HBM_PEAK_GBPS, 4))
+        kernels[c.name] = ent
+    dom = max(calls, key=lambda c: sum(c.times_ms))
+    avg = sum(dom.times_ms) / len(dom.times_ms) * 1e-3
+    if dom.kind == "gemm":
+        ach = dom.flops / avg / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / FP8_PEAK_TFLOPS, 4)}
+    else:
+        ach = dom.nbytes / avg / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4)}
+    roof["kernel"] = dom.name
+    roof["traffic"] = load_traffic(f"{args.config}:{dom.name}", dom.kind)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "pct_of_fp8_dense_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded, shapes and distributions of the configuration)",
+        "config": desc,
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline and data is not None:
+        out["cpu_baseline"] = cpu_baseline(args.config, data, args.cpu_sample_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

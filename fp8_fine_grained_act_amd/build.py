@@ -21,6 +21,9 @@ FLAGS = [
     "-ffp-contract=off",
     # keep the compiler from forming packed FP32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs (the per-block rescale reads them at once;
+    # the AGPR form would add an accvgpr read per result element)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
 

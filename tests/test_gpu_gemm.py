@@ -91,7 +91,8 @@ def test_fprop_strided_output_and_determinism(gpu_lib):
     torch.cuda.synchronize()
     assert torch.equal(big[:, :n], again)
     assert torch.count_nonzero(big[:, n:]) == 0
-    assert_gemm_parity(bf16_values_host(again), gemm_fprop(qa, sa, qb, sb), label="strided")
+    mag = gemm_fprop(magnitude_codes(qa), sa, magnitude_codes(qb), sb)
+    assert_gemm_parity(bf16_values_host(again), gemm_fprop(qa, sa, qb, sb), mag, label="strided")
 
 
 # ---------------------------------------------------------------- dgrad -------
@@ -139,9 +140,10 @@ def test_wgrad_random_codes_ragged_and_accumulate(gpu_lib):
         args = (to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb))
         c = gpu_lib.fp8bs_gemm_wgrad(*args)
         c64 = gemm_wgrad(qa, sa, qb, sb)
-        assert_gemm_parity(c.cpu().numpy(), c64, out_bf16=False, label=f"wgrad {m}x{n}x{t}")
+        mag = gemm_wgrad(magnitude_codes(qa), sa, magnitude_codes(qb), sb)
+        assert_gemm_parity(c.cpu().numpy(), c64, mag, out_bf16=False, label=f"wgrad {m}x{n}x{t}")
         gpu_lib.fp8bs_gemm_wgrad(*args, c=c, accumulate=1)
-        assert_gemm_parity(c.cpu().numpy(), 2 * c64, out_bf16=False, label="wgrad accumulate")
+        assert_gemm_parity(c.cpu().numpy(), 2 * c64, 2 * mag, out_bf16=False, label="wgrad accumulate")
 
 
 def test_wgrad_c5_sampled_block(gpu_lib):
@@ -160,7 +162,8 @@ def test_wgrad_c5_sampled_block(gpu_lib):
     oqdy, osdy = quantize_act_1x128_t(np.ascontiguousarray(d["dy"][:, rows]))
     oqx, osx = quantize_act_1x128_t(np.ascontiguousarray(d["x"][:, cols]))
     c64 = gemm_wgrad(oqdy, osdy, oqx, osx)
-    assert_gemm_parity(got, c64, out_bf16=False, label="c5")
+    mag = gemm_wgrad(magnitude_codes(oqdy), osdy, magnitude_codes(oqx), osx)
+    assert_gemm_parity(got, c64, mag, out_bf16=False, label="c5")
 
 
 # ---------------------------------------------------------------- grouped -----
@@ -207,7 +210,8 @@ def test_grouped_empty_and_single_expert(gpu_lib):
         c = gpu_lib.fp8bs_grouped_gemm(to_dev(qa), to_dev(sa), to_dev(off.astype(np.int32)), to_dev(qb),
                                        to_dev(sb))
         c64 = grouped_gemm(qa, sa, off, qb, sb)
-        assert_gemm_parity(bf16_values_host(c), c64, label=f"grouped offsets {off.tolist()}")
+        mag = grouped_gemm(magnitude_codes(qa), sa, off, magnitude_codes(qb), sb)
+        assert_gemm_parity(bf16_values_host(c), c64, mag, label=f"grouped offsets {off.tolist()}")
 
 
 def test_grouped_c4_full_launch_sampled_experts(gpu_lib):
@@ -233,6 +237,7 @@ def test_grouped_c4_full_launch_sampled_experts(gpu_lib):
         oqa, osa = quantize_act_1x128(g["x"][rows])
         c64 = gemm_fprop(oqa, osa, oqb, osb)
         realm = rows < lo + cnt
-        assert_gemm_parity(got[realm], c64[realm], label=f"c4 expert {e}")
+        mag = gemm_fprop(magnitude_codes(oqa), osa, magnitude_codes(oqb), osb)
+        assert_gemm_parity(got[realm], c64[realm], mag[realm], label=f"c4 expert {e}")
         assert np.all(got[~realm] == 0)
     del w

@@ -83,7 +83,7 @@ def test_act_rows_every_finite_bf16_value(gpu_lib):
     finite = (pats & 0x7F80) != 0x7F80
     pats = pats[finite].astype(np.uint16)
     rng.shuffle(pats)
-    n_tiles = (pats.size + 126) // 127
+    n_tiles = ((pats.size + 126) // 127 + 7) // 8 * 8         # whole 1024-wide rows
     bits = np.zeros((n_tiles, 128), np.uint16)
     flat = np.zeros(n_tiles * 127, np.uint16)
     flat[:pats.size] = pats

@@ -27,6 +27,7 @@ from .configs import CONFIGS, config_by_name
 from .gen import (
     f32_to_bf16_bits,
     gemm_inputs,
+    layer_inputs,
     wgrad_inputs,
     moe_routing,
     grouped_inputs_host,
@@ -35,6 +36,6 @@ from .gen import (
 )
 
 __all__ = [
-    "CONFIGS", "config_by_name", "f32_to_bf16_bits", "gemm_inputs", "wgrad_inputs",
+    "CONFIGS", "config_by_name", "f32_to_bf16_bits", "gemm_inputs", "layer_inputs", "wgrad_inputs",
     "moe_routing", "grouped_inputs_host", "device_expert_weights", "normal_bf16",
 ]

@@ -15,8 +15,8 @@ def f32_to_bf16_bits(x):
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
 
 
-def _streams(seed):
-    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(4)]
+def _streams(seed, count=4):
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(count)]
 
 
 def normal_bf16(rng, shape, std):
@@ -51,6 +51,22 @@ def gemm_inputs(name_or_cfg, **override):
     del a
     b_bits = normal_bf16(rng_b, (n, k), cfg.get("b_std", 0.02))
     return dict(a=a_bits, b=b_bits, outlier_cols=cols)
+
+
+def layer_inputs(name_or_cfg, dy_std=1e-3, **override):
+    """Forward-GEMM inputs plus an output gradient dY [M, N] ~ N(0, dy_std).
+
+    For a training pass of one linear layer: forward Y = X W^T, activation
+    gradient dX = dY W, weight gradient dW = dY^T X.  dY comes from a fifth
+    stream of the same seed, so A and B are identical to ``gemm_inputs``.
+    Returns dict(a=X [M,K], b=W [N,K], dy=[M,N]) as bf16 bits.
+    """
+    cfg = config_by_name(name_or_cfg) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
+    cfg.update(override)
+    d = gemm_inputs(cfg)
+    rng_dy = _streams(cfg["seed"], 5)[4]
+    d["dy"] = normal_bf16(rng_dy, (cfg["M"], cfg["N"]), dy_std)
+    return d
 
 
 def wgrad_inputs(name_or_cfg, **override):
