@@ -10,6 +10,7 @@ namespace fp8bs {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = 128;           // scale-group length along the contraction
 constexpr float kE4M3Max = 448.0f;

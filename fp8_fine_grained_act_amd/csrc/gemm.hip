@@ -26,8 +26,13 @@
 //     rows m): each lane ends with one output row and four consecutive output
 //     columns -- one 8-byte (bf16) or 16-byte (f32) store.
 //   * dgrad reads the forward weight as stored ([K, N], N contiguous): its
-//     slab goes through registers and is byte-transposed (v_perm) on its way
-//     into LDS so that the MFMA sees K-contiguous rows.
+//     slab is copied as is (LDS rows = k) and the MFMA fragments, which need 32
+//     consecutive k per lane, are gathered with ds_read_b64_tr_b8 (gfx950's
+//     transposing LDS read).  Within a 16-lane group that instruction hands
+//     lane i byte (i mod 8) of the 8-byte words read by lanes (i div 8) + 2b,
+//     b = 0..7; pointing even lanes at 8 consecutive k rows of columns n..n+7
+//     and odd lanes at the same rows of columns n+8..n+15 leaves lane i with 8
+//     consecutive k of column n + i.
 
 #include "common.h"
 #include "launch.h"
@@ -71,20 +76,6 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32
 // swizzled byte offset of 16-byte chunk `chunk` of LDS row `row`
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
 
-// 4x4 byte transpose: rows r0..r3 (4 bytes each) -> column dwords o0..o3,
-// o_j = (r0.b_j, r1.b_j, r2.b_j, r3.b_j).
-__device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
-                                             uint32_t& o0, uint32_t& o1, uint32_t& o2, uint32_t& o3) {
-  uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
-  uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
-  uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
-  uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
-  o0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-  o1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-  o2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-  o3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
-}
-
 // wait until at most n vector-memory operations of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -111,7 +102,7 @@ void gemm_kernel(GemmArgs p) {
   static_assert(A_CP * kThreads * 16 == BM * BK && B_CP * kThreads * 16 == BN * BK, "copy split");
   static_assert(BM == 128 && BN == 128, "staging split assumes a 128 x 128 tile");
   // vector-memory operations one wave issues per slab (waited on by count)
-  constexpr int kSlabOps = A_CP + (MODE == kDgrad ? 4 : B_CP) + 1;
+  constexpr int kSlabOps = A_CP + B_CP + 1;
 
   __shared__ __attribute__((aligned(16))) Smem<BM, BN> sm[STAGES];
 
@@ -148,7 +139,7 @@ void gemm_kernel(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa + m0 * nkb, rows_a * nkb * 4);
   __amdgpu_buffer_rsrc_t rb, rsb;
   if (MODE == kDgrad) {
-    rb = make_rsrc(qb, K * N);
+    rb = make_rsrc(qb + n0, K * N - n0);
     rsb = make_rsrc(sb, (K / 128) * (N / 128) * 4);
   } else if (MODE == kWgrad) {
     rb = make_rsrc(qb + n0 * K, rows_b * K);
@@ -170,27 +161,18 @@ void gemm_kernel(GemmArgs p) {
   for (int i = 0; i < B_CP; ++i) {
     const int c = (i * 4 + wave) * 64 + lane;
     const int row = c >> 3, pc = c & 7;
-    boff[i] = (uint32_t)(row * K + ((pc ^ (row & 7)) << 4));
+    const int64_t ld = MODE == kDgrad ? N : K;      // dgrad: slab rows are k, ld = N
+    boff[i] = (uint32_t)(row * ld + ((pc ^ (row & 7)) << 4));
   }
-
-  // dgrad: this thread's 4 (k) x 16 (n) byte patch of the [K, N] weight slab
-  const int dlr = tid >> 3, dlc = tid & 7;
-  uint4 rbd[4];
 
   auto issue_slab = [&](int kb, Smem<BM, BN>& s) {
     const uint32_t ks = (uint32_t)kb * BK;
 #pragma unroll
     for (int i = 0; i < A_CP; ++i) dma16(ra, s.a + (i * 4 + wave) * 1024, aoff[i], ks);
-    if (MODE == kDgrad) {
+    {
+      const uint32_t kso = MODE == kDgrad ? ks * (uint32_t)N : ks;   // dgrad: K-block = 128 rows of [K, N]
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        rbd[q] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       rb, (int)((uint32_t)(4 * dlr + q) * (uint32_t)N + (uint32_t)n0 + 16u * dlc),
-                       (int)(ks * (uint32_t)N), 0));
-    } else {
-#pragma unroll
-      for (int i = 0; i < B_CP; ++i) dma16(rb, s.b + (i * 4 + wave) * 1024, boff[i], ks);
+      for (int i = 0; i < B_CP; ++i) dma16(rb, s.b + (i * 4 + wave) * 1024, boff[i], kso);
     }
     // scales of this K block: exactly one 4-byte-per-lane copy per wave, so every
     // wave has the same number of copies in flight per slab
@@ -205,22 +187,6 @@ void gemm_kernel(GemmArgs p) {
       const uint32_t idx = MODE == kDgrad ? (uint32_t)kb * (uint32_t)(N / 128) + nb0
                                           : nb0 * (uint32_t)nkb + (uint32_t)kb;
       dma4(rsb, s.sb + (wave - 2) * 64, 0u, idx * 4u);
-    }
-  };
-
-  auto store_dgrad_slab = [&](Smem<BM, BN>& s) {
-    const int kofs = 4 * dlr;
-    const int kchunk = kofs >> 4, kin = kofs & 15;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t o[4];
-      auto get = [&](const uint4& v) { return d == 0 ? v.x : (d == 1 ? v.y : (d == 2 ? v.z : v.w)); };
-      transpose4x4(get(rbd[0]), get(rbd[1]), get(rbd[2]), get(rbd[3]), o[0], o[1], o[2], o[3]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int nr = 16 * dlc + 4 * d + j;
-        *reinterpret_cast<uint32_t*>(&s.b[swz(nr, kchunk) + kin]) = o[j];
-      }
     }
   };
 
@@ -248,10 +214,24 @@ void gemm_kernel(GemmArgs p) {
     }
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
-      const int r = WN * wn + 16 * i + l16;
-      const uint4 lo = *reinterpret_cast<const uint4*>(&s.b[swz(r, 2 * g)]);
-      const uint4 hi = *reinterpret_cast<const uint4*>(&s.b[swz(r, 2 * g + 1)]);
-      f.bf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if (MODE == kDgrad) {
+        // rows of s.b are k; lane (g, l16) needs k = 32g .. 32g+31 of column WN*wn + 16i + l16
+        const int col16 = (WN * wn + 16 * i) >> 4;       // 16-byte chunk of the columns
+        const int half = (l16 & 1) << 3;                 // odd lanes: columns +8 .. +15
+        v2i part[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 32 * g + 8 * q + (l16 >> 1);
+          part[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) v2i*)(&s.b[swz(row, col16) + half]));
+        }
+        f.bf[i] = v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
+      } else {
+        const int r = WN * wn + 16 * i + l16;
+        const uint4 lo = *reinterpret_cast<const uint4*>(&s.b[swz(r, 2 * g)]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(&s.b[swz(r, 2 * g + 1)]);
+        f.bf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
     }
 #pragma unroll
     for (int j = 0; j < TM; ++j) f.wa[j] = s.sa[WM * wm + 16 * j + l16];
@@ -301,15 +281,8 @@ void gemm_kernel(GemmArgs p) {
   };
 
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
-    if (s < nkb) {
-      issue_slab(s, sm[s]);
-      if (MODE == kDgrad) {
-        wait_vmcnt<0>();
-        store_dgrad_slab(sm[s]);
-      }
-    }
-  }
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nkb) issue_slab(s, sm[s]);
 
   for (int kb0 = 0; kb0 < nkb; kb0 += STAGES) {
 #pragma unroll
@@ -318,15 +291,11 @@ void gemm_kernel(GemmArgs p) {
       if (kb < nkb) {
         const int nxt = kb + STAGES - 1;
         const int ns = (s + STAGES - 1) % STAGES;
-        publish(MODE != kDgrad && kb + STAGES - 2 < nkb);
+        publish(kb + STAGES - 2 < nkb);
         Frags f;
         load_frags(sm[s], f);
         if (nxt < nkb) issue_slab(nxt, sm[ns]);
         mfma_phase(f);
-        if (MODE == kDgrad && nxt < nkb) {
-          wait_vmcnt<0>();
-          store_dgrad_slab(sm[ns]);
-        }
       }
     }
   }
