@@ -12,16 +12,20 @@
 // products span many binades); the FP32 promotion bounds how far that error
 // can accumulate, as on the pages' hardware.
 //
-// Structure of one workgroup (4 waves in a 2x2 grid, each wave a
-// (BM/2) x (BN/2) patch of 16x16 MFMA tiles):
+// Structure of one workgroup (WAVES_M x WAVES_N waves, each wave a
+// (BM/WAVES_M) x (BN/WAVES_N) patch of 16x16 MFMA tiles):
 //   * K is walked in 128-deep slabs.  A slab of A (BM rows x 128 bytes), of B
-//     (BN rows x 128 bytes) and of the scales that go with it is copied from
-//     memory straight into LDS with buffer_load ... lds (16 bytes per lane),
-//     STAGES slabs in flight, so no VGPRs hold staged data and rows past the
-//     matrix edge read as zero (buffer range check).
-//   * LDS rows are 128 bytes; their 16-byte chunks are XOR-swizzled with the
-//     row index (applied to the global address of the copy), so the fragment
-//     reads (two ds_read_b128 per 16x128 operand) hit distinct banks.
+//     and of the scales that go with it is copied from memory straight into
+//     LDS with buffer_load ... lds (16 or 4 bytes per lane), STAGES slabs in
+//     flight; no VGPRs hold staged data, and rows past the matrix edge read as
+//     zero (buffer range check).  Each stage is its own LDS object, so the
+//     compiler can tell a slab being filled from the slab being read.
+//   * The MFMA operands of slab k+1 are read from LDS into a second register
+//     set while the MFMAs of slab k run (register double buffering), so LDS
+//     latency sits under matrix-core time.
+//   * LDS rows are 128 bytes of 16-byte chunks; chunk c of row r is stored at
+//     chunk c ^ ((r >> 1) & 7).  A 16-lane pass of ds_read_b128 then reads 16
+//     distinct 16-byte bank groups (two rows fill the 64 banks).
 //   * MFMA src0 carries B rows (output columns n), src1 carries A rows (output
 //     rows m): each lane ends with one output row and four consecutive output
 //     columns -- one 8-byte (bf16) or 16-byte (f32) store.
@@ -51,12 +55,11 @@ struct GemmArgs {
   int64_t m, n, k;
   const int32_t* seg;
   int64_t num_experts;
-  int64_t tiles_n;
+  int64_t tiles_m, tiles_n;
   int accumulate;
 };
 
 constexpr int BK = 128;
-constexpr int kThreads = 256;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access, gfx9 family
 
 typedef __attribute__((address_space(3))) void lds_ptr_t;
@@ -73,47 +76,87 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)lds, 4, (int)voff, (int)soff, 0, 0);
 }
 
-// swizzled byte offset of 16-byte chunk `chunk` of LDS row `row`
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+// byte offset of 16-byte chunk `chunk` of LDS row `row` (rows of 128 bytes)
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
 
-// wait until at most n vector-memory operations of this wave are outstanding
+// s_waitcnt with only a vmcnt limit (expcnt, lgkmcnt left unconstrained)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
+// wave-uniform runtime limit: a chain of scalar compares picks the immediate
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n >= N) {
+    wait_vmcnt<N>();
+  } else if constexpr (N > 0) {
+    wait_vmcnt_le<N - 1>(n);
+  }
+}
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) { wait_vmcnt_le<47>(n); }
 
 template <int BM, int BN>
-struct Smem {
+struct Stage {
   uint8_t a[BM * BK];
   uint8_t b[BN * BK];
   float sa[BM];
   float sb[BN];
 };
 
-template <int MODE, int BM, int BN, int STAGES>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void gemm_kernel(GemmArgs p) {
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile");
-  constexpr int WM = BM / 2, WN = BN / 2;         // wave patch
-  constexpr int TM = WM / 16, TN = WN / 16;       // MFMA tiles per wave
-  constexpr int A_CP = BM * BK / (kThreads * 16); // 16-byte copies per thread per A slab
-  constexpr int B_CP = BN * BK / (kThreads * 16);
-  static_assert(A_CP * kThreads * 16 == BM * BK && B_CP * kThreads * 16 == BN * BK, "copy split");
-  static_assert(BM == 128 && BN == 128, "staging split assumes a 128 x 128 tile");
-  // vector-memory operations one wave issues per slab (waited on by count)
-  constexpr int kSlabOps = A_CP + B_CP + 1;
+// One LDS object per pipeline stage (a separate variable per IDX), so the
+// compiler's alias information separates the stage being filled by DMA from
+// the stage being read.
+template <int BM, int BN, int IDX>
+__device__ __forceinline__ Stage<BM, BN>& lds_stage() {
+  __shared__ __attribute__((aligned(16))) Stage<BM, BN> st;
+  return st;
+}
 
-  __shared__ __attribute__((aligned(16))) Smem<BM, BN> sm[STAGES];
+template <int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+struct GemmCfg {
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave patch
+  static constexpr int TM = WM / 16, TN = WN / 16;              // MFMA tiles per wave
+  // copies per slab: every wave issues A_CP copies of 8 A rows and B_CP copies
+  // of 8 B rows (dgrad: 8 k-rows of the [K, N] slab), 1 KB each; the
+  // kScaleJobs 64-entry scale copies (A rows first, then B columns) go to
+  // waves 0, 1, ... round-robin
+  static constexpr int A_CP = BM / 8 / kWaves;
+  static constexpr int B_CP = BN / 8 / kWaves;
+  static constexpr int kScaleJobs = (BM + BN) / 64;
+  static constexpr int kScaleRounds = (kScaleJobs + kWaves - 1) / kWaves;
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave patch must be whole MFMA tiles");
+  static_assert(A_CP * 8 * kWaves == BM && B_CP * 8 * kWaves == BN, "copies must split evenly over waves");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "scale copies cover 64 rows each");
+  static_assert(MODE != kDgrad || BN == 128, "dgrad slab rows are 128 columns wide");
+  static_assert(STAGES == 2 || STAGES == 3, "pipeline depth");
+  static_assert((STAGES - 1) * (A_CP + B_CP + kScaleRounds) <= 47, "copies in flight must fit the vmcnt waits");
+  static __device__ __forceinline__ int jobs_of(int wave) {
+    return A_CP + B_CP + kScaleJobs / kWaves + (wave < kScaleJobs % kWaves ? 1 : 0);
+  }
+};
+
+template <int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool DBUF>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void gemm_kernel(GemmArgs p) {
+  using C = GemmCfg<MODE, BM, BN, WAVES_M, WAVES_N, STAGES>;
+  constexpr int WM = C::WM, WN = C::WN, TM = C::TM, TN = C::TN;
+  constexpr int NW = C::kWaves;
+
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int l16 = lane & 15, g = lane >> 4;
 
+  // tile order: consecutive workgroups walk down M inside one N column, so a
+  // column of B stays hot in L2 while the A rows stream past
   const int64_t tile = blockIdx.x;
-  const int64_t tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+  const int64_t tn = tile / p.tiles_m, tm = tile - tn * p.tiles_m;
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t M = p.m, N = p.n, K = p.k;
   const int nkb = (int)(K / BK);
@@ -149,62 +192,56 @@ void gemm_kernel(GemmArgs p) {
     rsb = make_rsrc(sb, (N / 128) * nkb * 4);
   }
 
-  // per-thread copy offsets (without the K-block term), swizzle on the global side
-  uint32_t aoff[A_CP], boff[B_CP];
-#pragma unroll
-  for (int i = 0; i < A_CP; ++i) {
-    const int c = (i * 4 + wave) * 64 + lane;   // 16-byte chunk index inside the slab
-    const int row = c >> 3, pc = c & 7;
-    aoff[i] = (uint32_t)(row * K + ((pc ^ (row & 7)) << 4));
-  }
-#pragma unroll
-  for (int i = 0; i < B_CP; ++i) {
-    const int c = (i * 4 + wave) * 64 + lane;
-    const int row = c >> 3, pc = c & 7;
-    const int64_t ld = MODE == kDgrad ? N : K;      // dgrad: slab rows are k, ld = N
-    boff[i] = (uint32_t)(row * ld + ((pc ^ (row & 7)) << 4));
-  }
-
-  auto issue_slab = [&](int kb, Smem<BM, BN>& s) {
+  // ---- one slab's copies ------------------------------------------------------
+  auto issue_slab = [&](int kb, Stage<BM, BN>& s) {
     const uint32_t ks = (uint32_t)kb * BK;
 #pragma unroll
-    for (int i = 0; i < A_CP; ++i) dma16(ra, s.a + (i * 4 + wave) * 1024, aoff[i], ks);
-    {
-      const uint32_t kso = MODE == kDgrad ? ks * (uint32_t)N : ks;   // dgrad: K-block = 128 rows of [K, N]
-#pragma unroll
-      for (int i = 0; i < B_CP; ++i) dma16(rb, s.b + (i * 4 + wave) * 1024, boff[i], kso);
+    for (int i = 0; i < C::A_CP; ++i) {
+      const int j = i * NW + wave;
+      const int c = j * 64 + lane, row = c >> 3, pc = c & 7;
+      const int lc = pc ^ ((row >> 1) & 7);
+      dma16(ra, s.a + j * 1024, (uint32_t)(row * K + (lc << 4)), ks);
     }
-    // scales of this K block: exactly one 4-byte-per-lane copy per wave, so every
-    // wave has the same number of copies in flight per slab
-    if (wave < 2) {
-      dma4(rsa, s.sa + wave * 64, (uint32_t)((wave * 64 + lane) * nkb) * 4u, (uint32_t)kb * 4u);
-    } else if (MODE == kWgrad) {
-      const int wv = wave - 2;
-      dma4(rsb, s.sb + wv * 64, (uint32_t)((wv * 64 + lane) * nkb) * 4u, (uint32_t)kb * 4u);
-    } else {
-      // the tile's single weight-block scale, broadcast to every lane's slot
-      const uint32_t nb0 = (uint32_t)(n0 / 128);
-      const uint32_t idx = MODE == kDgrad ? (uint32_t)kb * (uint32_t)(N / 128) + nb0
-                                          : nb0 * (uint32_t)nkb + (uint32_t)kb;
-      dma4(rsb, s.sb + (wave - 2) * 64, 0u, idx * 4u);
+#pragma unroll
+    for (int i = 0; i < C::B_CP; ++i) {
+      const int j = i * NW + wave;
+      const int c = j * 64 + lane, row = c >> 3, pc = c & 7;
+      const int lc = pc ^ ((row >> 1) & 7);
+      if (MODE == kDgrad)
+        dma16(rb, s.b + j * 1024, (uint32_t)(row * N + (lc << 4)), ks * (uint32_t)N);
+      else
+        dma16(rb, s.b + j * 1024, (uint32_t)(row * K + (lc << 4)), ks);
+    }
+#pragma unroll
+    for (int r = 0; r < C::kScaleRounds; ++r) {
+      const int js = r * NW + wave;
+      if (js < C::kScaleJobs) {
+        const int q = js * 64 + lane;            // scale slot: [0, BM) rows of A, [BM, BM+BN) columns
+        if (js * 64 < BM) {
+          dma4(rsa, s.sa + js * 64, (uint32_t)(q * nkb) * 4u, (uint32_t)kb * 4u);
+        } else {
+          const int col = q - BM;
+          float* dst = s.sb + (js * 64 - BM);
+          if (MODE == kWgrad) {
+            dma4(rsb, dst, (uint32_t)(col * nkb) * 4u, (uint32_t)kb * 4u);
+          } else {
+            // weight-block scale of this column (clipped to the last block past the edge)
+            const int64_t nb = min((n0 + col) / 128, N / 128 - 1);
+            const uint32_t idx = MODE == kDgrad ? (uint32_t)(kb * (N / 128) + nb) : (uint32_t)(nb * nkb + kb);
+            dma4(rsb, dst, idx * 4u, 0u);
+          }
+        }
+      }
     }
   };
 
-  v4f acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // Fragments of one slab: every LDS read of the slab happens here, before the
-  // next slab's copies are issued, so the copies never wait behind these reads
-  // and the MFMA phase below touches registers only.
+  // ---- operand fragments of one slab -----------------------------------------
   struct Frags {
     v8i af[TM], bf[TN];
     float wa[TM];
     v4f wb[TN];
   };
-  auto load_frags = [&](const Smem<BM, BN>& s, Frags& f) {
+  auto load_frags = [&](const Stage<BM, BN>& s, Frags& f) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int r = WM * wm + 16 * j + l16;
@@ -216,8 +253,8 @@ void gemm_kernel(GemmArgs p) {
     for (int i = 0; i < TN; ++i) {
       if (MODE == kDgrad) {
         // rows of s.b are k; lane (g, l16) needs k = 32g .. 32g+31 of column WN*wn + 16i + l16
-        const int col16 = (WN * wn + 16 * i) >> 4;       // 16-byte chunk of the columns
-        const int half = (l16 & 1) << 3;                 // odd lanes: columns +8 .. +15
+        const int col16 = (WN * wn + 16 * i) >> 4;
+        const int half = (l16 & 1) << 3;               // odd lanes: columns +8 .. +15
         v2i part[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -240,11 +277,17 @@ void gemm_kernel(GemmArgs p) {
       if (MODE == kWgrad) {
         f.wb[i] = *reinterpret_cast<const v4f*>(&s.sb[WN * wn + 16 * i + 4 * g]);
       } else {
-        const float v = s.sb[0];
+        const float v = s.sb[WN * wn + 16 * i];
         f.wb[i] = v4f{v, v, v, v};
       }
     }
   };
+
+  v4f acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   auto mfma_phase = [&](const Frags& f) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -265,37 +308,70 @@ void gemm_kernel(GemmArgs p) {
     }
   };
 
-  // ---- main loop: STAGES slabs in flight -------------------------------------
-  // LDS hand-off: a wave waits for its own copies of the slab it is about to
-  // read (vmcnt, counting only the newer slabs still allowed in flight) and for
-  // its own LDS writes (lgkmcnt), then the workgroup barrier publishes every
-  // wave's part.  The barrier also guarantees that the stage about to be
-  // refilled is no longer being read.
-  auto publish = [&](bool newer_in_flight) {
-    if (newer_in_flight) wait_vmcnt<(STAGES - 2) * kSlabOps>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's ds_write done
+  // ---- pipeline ----------------------------------------------------------------
+  // Hand-off of a slab: each wave waits for its own copies of that slab (newer
+  // slabs may stay in flight) and for its own LDS reads, then the barrier makes
+  // every wave's copies visible and guarantees that no wave still reads the
+  // stage that is refilled next.
+  const int my_jobs = C::jobs_of(wave);
+  auto publish = [&](int newer_slabs_in_flight) {
+    wait_vmcnt_dyn(newer_slabs_in_flight * my_jobs);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  auto stage_ref = [&](int s) -> Stage<BM, BN>& {
+    if (STAGES == 3 && s == 2) return lds_stage<BM, BN, (STAGES == 3 ? 2 : 1)>();
+    return s == 0 ? lds_stage<BM, BN, 0>() : lds_stage<BM, BN, 1>();
+  };
 
+  // prologue: slabs 0 .. STAGES-1 in flight
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nkb) issue_slab(s, sm[s]);
+  for (int s = 0; s < STAGES; ++s)
+    if (s < nkb) issue_slab(s, stage_ref(s));
 
-  for (int kb0 = 0; kb0 < nkb; kb0 += STAGES) {
+  if (DBUF) {
+    // slab kb's fragments sit in fr[kb & 1]; iteration kb reads slab kb+1's into
+    // the other set, refills the stage slab kb lived in with slab kb+STAGES,
+    // then runs slab kb's MFMAs (LDS latency under matrix-core time)
+    Frags fr[2];
+    publish(min(STAGES - 1, nkb - 1));
+    load_frags(stage_ref(0), fr[0]);
+    for (int kb0 = 0; kb0 < nkb; kb0 += 2 * STAGES) {
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) {
-      const int kb = kb0 + s;
-      if (kb < nkb) {
-        const int nxt = kb + STAGES - 1;
-        const int ns = (s + STAGES - 1) % STAGES;
-        publish(kb + STAGES - 2 < nkb);
-        Frags f;
-        load_frags(sm[s], f);
-        if (nxt < nkb) issue_slab(nxt, sm[ns]);
-        mfma_phase(f);
+      for (int u = 0; u < 2 * STAGES; ++u) {
+        const int kb = kb0 + u;
+        if (kb < nkb) {
+          const int s_cur = u % STAGES, s_nxt = (u + 1) % STAGES;
+          if (kb + 1 < nkb) {
+            publish(min(STAGES - 2, nkb - kb - 2));
+            load_frags(stage_ref(s_nxt), fr[(u + 1) & 1]);
+          }
+          // every wave passed the barrier above after reading slab kb's
+          // fragments, so stage s_cur is free
+          if (kb + STAGES < nkb) issue_slab(kb + STAGES, stage_ref(s_cur));
+          mfma_phase(fr[u & 1]);
+        }
+      }
+    }
+  } else {
+    // single fragment set: publish slab kb, read its fragments, refill the
+    // stage of slab kb-1 (read by every wave before this barrier), run MFMAs
+    for (int kb0 = 0; kb0 < nkb; kb0 += STAGES) {
+#pragma unroll
+      for (int u = 0; u < STAGES; ++u) {
+        const int kb = kb0 + u;
+        if (kb < nkb) {
+          // slabs issued so far: 0 .. STAGES-1 (prologue) and kb-2+STAGES
+          // (refills), so slab kb has min(STAGES-1 (first) or STAGES-2, rest)
+          // newer copies behind it
+          publish(kb == 0 ? min(STAGES - 1, nkb - 1) : min(STAGES - 2, nkb - kb - 1));
+          Frags f;
+          load_frags(stage_ref(u), f);
+          if (kb >= 1 && kb - 1 + STAGES < nkb) issue_slab(kb - 1 + STAGES, stage_ref((u + STAGES - 1) % STAGES));
+          mfma_phase(f);
+        }
       }
     }
   }
@@ -308,8 +384,8 @@ void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       const int64_t col = n0 + WN * wn + 16 * i + 4 * g;
+      if (col >= N) continue;
       if (MODE == kWgrad) {
-        if (col >= N) continue;
         float* dst = reinterpret_cast<float*>(p.c) + row * p.ldc + col;
         float4 o = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         if (p.accumulate) {
@@ -328,13 +404,14 @@ void gemm_kernel(GemmArgs p) {
   }
 }
 
-template <int MODE, int BM, int BN, int STAGES>
+template <int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool DBUF>
 static int launch_gemm(GemmArgs a, hipStream_t s) {
   a.tiles_n = (a.n + BN - 1) / BN;
-  const int64_t tiles_m = (a.m + BM - 1) / BM;
-  const int64_t grid = tiles_m * a.tiles_n;
+  a.tiles_m = (a.m + BM - 1) / BM;
+  const int64_t grid = a.tiles_m * a.tiles_n;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_kernel<MODE, BM, BN, STAGES>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<MODE, BM, BN, WAVES_M, WAVES_N, STAGES, DBUF>), dim3((unsigned)grid),
+                     dim3(64 * WAVES_M * WAVES_N), 0, s, a);
   return launch_status();
 }
 
@@ -346,6 +423,19 @@ using namespace fp8bs;
 // A or B, and the dgrad weight as a whole, must stay below 4 GiB.
 static bool fits_u32(int64_t bytes) { return bytes < 0xFFFFFFFFLL; }
 
+#ifndef FP8BS_TILE_FPROP
+#define FP8BS_TILE_FPROP 128, 128, 2, 2, 2, false
+#endif
+#ifndef FP8BS_TILE_DGRAD
+#define FP8BS_TILE_DGRAD 128, 128, 2, 2, 2, false
+#endif
+#ifndef FP8BS_TILE_WGRAD
+#define FP8BS_TILE_WGRAD 128, 128, 2, 2, 2, false
+#endif
+#ifndef FP8BS_TILE_GROUPED
+#define FP8BS_TILE_GROUPED 128, 128, 2, 2, 2, false
+#endif
+
 extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
                           int64_t m, int64_t n, int64_t k, int b_layout, uint16_t* c, int64_t ldc,
                           void* stream) {
@@ -356,9 +446,9 @@ extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb,
   if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
       ldc % 8)
     return FP8BS_ERR_ALIGN;
-  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, k, nullptr, 0, 0, 0};
-  if (b_layout == 0) return launch_gemm<kFprop, 128, 128, 2>(a, (hipStream_t)stream);
-  return launch_gemm<kDgrad, 128, 128, 2>(a, (hipStream_t)stream);
+  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, k, nullptr, 0, 0, 0, 0};
+  if (b_layout == 0) return launch_gemm<kFprop, FP8BS_TILE_FPROP>(a, (hipStream_t)stream);
+  return launch_gemm<kDgrad, FP8BS_TILE_DGRAD>(a, (hipStream_t)stream);
 }
 
 extern "C" int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int32_t* seg_offsets,
@@ -372,8 +462,8 @@ extern "C" int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int3
   if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
       !aligned(seg_offsets, 4))
     return FP8BS_ERR_ALIGN;
-  GemmArgs a{qa, sa, qb, sb, c, n, total_rows, n, k, seg_offsets, num_experts, 0, 0};
-  return launch_gemm<kGrouped, 128, 128, 2>(a, (hipStream_t)stream);
+  GemmArgs a{qa, sa, qb, sb, c, n, total_rows, n, k, seg_offsets, num_experts, 0, 0, 0};
+  return launch_gemm<kGrouped, FP8BS_TILE_GROUPED>(a, (hipStream_t)stream);
 }
 
 extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
@@ -386,6 +476,6 @@ extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_
   if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
       ldc % 4)
     return FP8BS_ERR_ALIGN;
-  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, t, nullptr, 0, 0, accumulate};
-  return launch_gemm<kWgrad, 128, 128, 2>(a, (hipStream_t)stream);
+  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, t, nullptr, 0, 0, 0, accumulate};
+  return launch_gemm<kWgrad, FP8BS_TILE_WGRAD>(a, (hipStream_t)stream);
 }
