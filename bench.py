@@ -47,6 +47,8 @@ def parse_args():
     p.add_argument("--rotate", type=int, default=0, help="input copies to rotate over (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=2048)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run plain 512 MiB device-to-device copies (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -267,6 +269,15 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        # a plain copy of known size: reads and writes 512 MiB each per launch
+        src = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel(), "launches": 4}), flush=True)
+        return
 
     if args.config in ("c2", "c3"):
         calls, state, desc, data = build_layer_step(lib, args.config, args.rotate)

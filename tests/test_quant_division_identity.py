@@ -1,0 +1,33 @@
+"""The HIP quantizers evaluate x / s with a per-tile reciprocal and one FMA
+correction step instead of a full division per element.  This CPU test proves
+the two give identical E4M3 codes for every pair of bf16 inputs the kernels
+send down that path (amax at or above the kernels' tiny-tile threshold), by
+exhaustive enumeration in C (gcc, IEEE fmaf)."""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "host", "recip_division_check.c")
+COMMON_H = os.path.join(os.path.dirname(HERE), "fp8_fine_grained_act_amd", "csrc", "common.h")
+
+
+def kernel_threshold():
+    text = open(COMMON_H, encoding="utf-8").read()
+    m = re.search(r"kTinyAmaxBits\s*=\s*(0x[0-9A-Fa-f]+)u", text)
+    assert m, "threshold constant not found in the kernel header"
+    return int(m.group(1), 16)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_reciprocal_correction_matches_ieee_division_exhaustively(tmp_path):
+    exe = tmp_path / "recip_division_check"
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-o", str(exe), SRC, "-lm"], check=True)
+    thr = kernel_threshold()
+    out = subprocess.run([str(exe), hex(thr)], capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "mismatches=0" in out.stdout
