@@ -12,9 +12,13 @@ included; this runs every step of the hot path except the MoE grouped GEMM):
 Other configurations (``--config c3|c4|c5``) print their own line.
 
 Inputs are resident in HBM before timing; the step rotates over several input
-copies (>= 256 MB in total) so the 256 MB Infinity Cache cannot hold them
-between steps.  Per-kernel durations come from HIP events recorded on the
-launch stream around every call of every timed step.
+copies (>= 512 MB in total) so the 256 MB Infinity Cache cannot hold them
+between steps.  Each step (one per input copy) is captured once into a HIP
+graph, so the timed steps run back to back without host launch gaps; a replay
+is checked bit for bit against the eager launches before timing.  Per-kernel
+durations come from a second timed region on the same stream: every call is
+captured ``--kernel-reps`` times in a row into a graph of its own (rotating
+over the input copies) and timed with HIP events around the replay.
 """
 
 import argparse
@@ -47,6 +51,8 @@ def parse_args():
     p.add_argument("--rotate", type=int, default=0, help="input copies to rotate over (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=4096)
+    p.add_argument("--kernel-reps", type=int, default=24, help="launches per per-kernel timing graph")
+    p.add_argument("--eager", action="store_true", help="time eager launches instead of step graphs")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 512 MiB device-to-device copies (reference for HBM byte counters)")
     return p.parse_args()
@@ -68,8 +74,9 @@ def dev_bf16(bits):
 
 
 class Call:
-    def __init__(self, name, kind, fn, flops=0.0, nbytes=0.0):
+    def __init__(self, name, kind, fn, flops=0.0, nbytes=0.0, outs=()):
         self.name, self.kind, self.fn, self.flops, self.nbytes = name, kind, fn, flops, nbytes
+        self.outs = list(outs)
         self.times_ms = []
 
 
@@ -105,22 +112,23 @@ def build_layer_step(lib, cfg_name, rotate):
     act_bytes = lambda r, c: r * c * 3 + r * c // 128 * 4  # noqa: E731
     calls = [
         Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(cur()[0], q=qx, scales=sx),
-             nbytes=act_bytes(m, k)),
+             nbytes=act_bytes(m, k), outs=(qx, sx)),
         Call("quant_w", "quant", lambda: lib.fp8bs_quantize_w_128x128(cur()[1], q=qw, scales=sw),
-             nbytes=n * k * 3 + (n // 128) * (k // 128) * 4),
-        Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k),
+             nbytes=n * k * 3 + (n // 128) * (k // 128) * 4, outs=(qw, sw)),
+        Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k,
+             outs=(y,)),
         Call("quant_act_dy", "quant", lambda: lib.fp8bs_quantize_act_1x128(cur()[2], q=qdy, scales=sdy),
-             nbytes=act_bytes(m, n)),
+             nbytes=act_bytes(m, n), outs=(qdy, sdy)),
         Call("gemm_dgrad", "gemm", lambda: lib.fp8bs_gemm(qdy, sdy, qw, sw, b_layout=1, c=dx),
-             flops=2.0 * m * n * k),
+             flops=2.0 * m * n * k, outs=(dx,)),
         Call("quant_act_dy_t", "quant",
              lambda: lib.fp8bs_quantize_act_1x128(cur()[2], transpose=1, q=qdyt, scales=sdyt),
-             nbytes=act_bytes(m, n)),
+             nbytes=act_bytes(m, n), outs=(qdyt, sdyt)),
         Call("quant_act_x_t", "quant",
              lambda: lib.fp8bs_quantize_act_1x128(cur()[0], transpose=1, q=qxt, scales=sxt),
-             nbytes=act_bytes(m, k)),
+             nbytes=act_bytes(m, k), outs=(qxt, sxt)),
         Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdyt, sdyt, qxt, sxt, c=dw),
-             flops=2.0 * m * n * k),
+             flops=2.0 * m * n * k, outs=(dw,)),
     ]
     desc = dict(workload=f"{cfg_name}: one FP8 training pass (forward + dgrad + wgrad, all quantization "
                          f"included) of a linear layer, {cfg['desc']}",
@@ -150,11 +158,11 @@ def build_grouped_step(lib, rotate):
     real = float(counts.sum())
     calls = [
         Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, q=qx, scales=sx),
-             nbytes=rows * k * 3 + rows * k // 128 * 4),
+             nbytes=rows * k * 3 + rows * k // 128 * 4, outs=(qx, sx)),
         Call("quant_w_experts", "quant", lambda: lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw),
-             nbytes=num_e * n * k * 3 + num_e * (n // 128) * (k // 128) * 4),
+             nbytes=num_e * n * k * 3 + num_e * (n // 128) * (k // 128) * 4, outs=(qw, sw)),
         Call("gemm_grouped", "gemm", lambda: lib.fp8bs_grouped_gemm(qx, sx, seg, qw, sw, c=y),
-             flops=2.0 * real * n * k),
+             flops=2.0 * real * n * k, outs=(y,)),
     ]
     desc = dict(workload="c4: MoE routed-expert forward, 4096 tokens x top-8 of 256 experts (Zipf 1.1), "
                          "fused gate+up N=4096, K=7168; quantize X and all expert weights, grouped GEMM",
@@ -180,35 +188,105 @@ def build_wgrad_step(lib, rotate):
     state = {"i": 0}
     calls = [
         Call("quant_act_dy_t", "quant", lambda: lib.fp8bs_quantize_act_1x128(dy, transpose=1, q=qdy, scales=sdy),
-             nbytes=t * m * 3 + t * m // 128 * 4),
+             nbytes=t * m * 3 + t * m // 128 * 4, outs=(qdy, sdy)),
         Call("quant_act_x_t", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, transpose=1, q=qx, scales=sx),
-             nbytes=t * n * 3 + t * n // 128 * 4),
-        Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdy, sdy, qx, sx, c=dw), flops=2.0 * m * n * t),
+             nbytes=t * n * 3 + t * n // 128 * 4, outs=(qx, sx)),
+        Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdy, sdy, qx, sx, c=dw), flops=2.0 * m * n * t,
+             outs=(dw,)),
     ]
     desc = dict(workload="c5: weight gradient dW[1536,7168] = dY^T X over 16384 tokens, both operands "
                          "transpose-quantized along tokens", T=t, M=m, N=n)
     return calls, state, desc, None
 
 
-def run_steps(calls, state, steps, record):
+def run_steps(calls, state, steps):
+    for _ in range(steps):
+        for c in calls:
+            c.fn()
+        state["i"] += 1
+
+
+def output_buffers(calls):
+    """Every output tensor of the step, without duplicates."""
+    seen, out = set(), []
+    for c in calls:
+        for v in c.outs:
+            if v.data_ptr() not in seen:
+                seen.add(v.data_ptr())
+                out.append(v)
+    return out
+
+
+def capture_steps(calls, state, rotate):
+    """One HIP graph per input copy, each holding one whole step."""
     import torch
 
-    evs = []
-    for _ in range(steps):
-        row = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(side):
+        for i in range(rotate):
+            state["i"] = i
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for c in calls:
+                    c.fn()
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    state["i"] = 0
+    return graphs
+
+
+def replay_matches_eager(calls, state, graphs):
+    """Run set 0 eagerly, then replay its graph over poisoned buffers: outputs must be bit-identical."""
+    import torch
+
+    bufs = output_buffers(calls)
+    state["i"] = 0
+    for c in calls:
+        c.fn()
+    torch.cuda.synchronize()
+    ref = [b.clone() for b in bufs]
+    for b in bufs:
+        b.view(torch.uint8).fill_(0xAB)
+    torch.cuda.synchronize()
+    graphs[0].replay()
+    torch.cuda.synchronize()
+
+    def bits(t):
+        return t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int16 if t.element_size() == 2
+                                                                         else torch.int32)
+    return all(torch.equal(bits(a), bits(b)) for a, b in zip(ref, bufs))
+
+
+def time_kernels(calls, state, rotate, reps):
+    """Average duration of each call: ``reps`` launches in one graph, HIP events around its replay."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out = []
+    with torch.cuda.stream(side):
         for c in calls:
-            if record:
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record()
-                c.fn()
-                b.record()
-                row.append((a, b))
-            else:
-                c.fn()
-        state["i"] += 1
-        evs.append(row)
-    return evs
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for r in range(reps):
+                    state["i"] = r % rotate
+                    c.fn()
+            g.replay()                       # warm
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(side)
+            g.replay()
+            b.record(side)
+            b.synchronize()
+            out.append(a.elapsed_time(b) / reps)
+            del g
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    state["i"] = 0
+    return out
 
 
 def cpu_baseline(cfg_name, data, sample_rows, min_seconds=10.0):
@@ -294,23 +372,41 @@ def main():
     else:
         calls, state, desc, data = build_wgrad_step(lib, args.rotate)
     torch.cuda.synchronize()
-
-    run_steps(calls, state, args.warmup, record=False)
+    rotate = desc.get("input_copies", 1)
+    run_steps(calls, state, 1)                       # first launches outside any capture
     torch.cuda.synchronize()
+    graphs, replay_ok = None, None
+    if not args.eager:
+        graphs = capture_steps(calls, state, rotate)
+        replay_ok = replay_matches_eager(calls, state, graphs)
+        if not replay_ok:
+            print("bench.py: a graph replay of the step differs from its eager launches", file=sys.stderr)
+            sys.exit(1)
 
-    # timed region: steps back to back, events around every call
+    def steps(n):
+        if graphs is None:
+            run_steps(calls, state, n)
+        else:
+            for _ in range(n):
+                graphs[state["i"] % rotate].replay()
+                state["i"] += 1
+
+    steps(args.warmup)
+    # timed region: K steps back to back
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    evs = run_steps(calls, state, args.steps, record=True)
+    steps(args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for row in evs:
-        for c, (a, b) in zip(calls, row):
-            c.times_ms.append(a.elapsed_time(b))
 
     ms_per_step = wall * 1e3 / args.steps
     gemm_flops = sum(c.flops for c in calls)
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    # per-kernel durations (second timed region, same stream discipline)
+    for c, ms in zip(calls, time_kernels(calls, state, rotate, args.kernel_reps)):
+        c.times_ms.append(ms)
+    kernel_sum_us = sum(c.times_ms[0] for c in calls) * 1e3
 
     kernels = {}
     for c in calls:
@@ -353,6 +449,9 @@ def main():
         "config": desc,
         "roofline": roof,
         "kernels": kernels,
+        "timing": {"step": "eager launches" if graphs is None else "one HIP graph per step (replay checked "
+                   "bit-identical to eager launches)", "kernel_sum_us": round(kernel_sum_us, 1),
+                   "kernel_reps": args.kernel_reps},
     }
     if not args.no_cpu_baseline and data is not None:
         out["cpu_baseline"] = cpu_baseline(args.config, data, args.cpu_sample_rows)
