@@ -15,12 +15,15 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 constexpr int kGroup = 128;           // scale-group length along the contraction
 constexpr float kE4M3Max = 448.0f;
 
-// Tiles whose amax (as bf16 bits, sign cleared) is below this take true IEEE
-// division for x / s.  Above it, x / s is evaluated as q0 = x*r, e = fma(-q0, s, x),
-// q = fma(e, r, q0) with r = 1/s correctly rounded (Markstein's correction step);
-// an exhaustive host check over every pair of bf16 values (amax, |x| <= amax)
-// shows that this gives the same E4M3 code as the IEEE quotient whenever
-// amax >= 2^-104.  0x1F80 is 2^-64, far inside that range.
+// x / s is evaluated as q0 = x*r, e = fma(-q0, s, x), q = fma(e, r, q0) with
+// r = 1/s correctly rounded (Markstein's correction step).  An exhaustive
+// host check over every pair of bf16 values (amax, |x| <= amax) shows that
+// this gives the same E4M3 code as the IEEE quotient whenever amax >= 2^-104.
+// Tiles whose amax (bf16 bits, sign cleared) is below kTinyAmaxBits (2^-64,
+// far inside that range) run the same step on x * 2^64 and s * 2^64: both
+// products are exact (s may be subnormal, s * 2^64 is normal), the quotient
+// is unchanged, and 1 / (s * 2^64) is finite; the same host check covers
+// every pair of that range.  A zero tile has s = r = 0, which yields q = 0.
 constexpr uint32_t kTinyAmaxBits = 0x1F80u;
 
 // ---- cross-lane max inside a row of 16 lanes (DPP, no LDS traffic) ----------
@@ -48,6 +51,13 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// lane-wise max of two pairs of 16-bit unsigned values (one v_pk_max_u16)
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
 // max of the two bf16 magnitudes held in one dword (sign bits cleared)
 __device__ __forceinline__ uint32_t absmax_pair(uint32_t x) {
   uint32_t a = x & 0x7FFF7FFFu;
@@ -57,49 +67,68 @@ __device__ __forceinline__ uint32_t absmax_pair(uint32_t x) {
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
+constexpr float kTinyScale = 0x1p64f;
+
 // Per-group quantization constants derived from the group's amax (bf16 bits).
 struct GroupScale {
-  float s;     // dequantization scale amax / 448 (IEEE division)
-  float r;     // 1 / s correctly rounded (0 when the slow path is taken)
-  bool slow;   // amax tiny or zero: use IEEE division per element
+  float s;     // dequantization scale amax / 448 (IEEE division), the stored scale
+  float d;     // divisor of the correction step: s, or s * 2^64 for a tiny tile
+  float r;     // 1 / d correctly rounded (0 for an all-zero tile)
+  bool slow;   // tiny tile: the values are multiplied by 2^64 first
 };
 
 __device__ __forceinline__ GroupScale group_scale(uint32_t amax_bits) {
   GroupScale g;
-  float amax = __uint_as_float(amax_bits << 16);
+  const float amax = __uint_as_float(amax_bits << 16);
   g.s = amax / kE4M3Max;
   g.slow = amax_bits < kTinyAmaxBits;
-  g.r = g.slow ? 0.0f : 1.0f / g.s;
+  g.d = g.slow ? g.s * kTinyScale : g.s;
+  g.r = g.d == 0.0f ? 0.0f : 1.0f / g.d;
   return g;
 }
 
-// |x| / s as the binary32 quotient, clamped to 448 (values in (448, 464) round
-// to 448 under RNE anyway; the quotient never exceeds 448 by more than a few ulp).
-__device__ __forceinline__ float scaled_mag(float a, const GroupScale& g) {
-  float q;
-  if (!g.slow) {
-    float q0 = a * g.r;
-    float e = __builtin_fmaf(-q0, g.s, a);
-    q = __builtin_fmaf(e, g.r, q0);
-  } else {
-    q = (g.s == 0.0f) ? 0.0f : a / g.s;
+// Quantize four bf16 values (two dwords, element 0 in the low half of x01)
+// into four E4M3 codes packed little-endian in one dword.  SLOW: tiny tile,
+// the magnitudes are scaled by 2^64 first.  No clamp is needed before the
+// E4M3 conversion: |x| <= amax keeps the quotient at most 448 * (1 + 2^-7)
+// even for a subnormal s (a few ulp above 448 otherwise), and
+// v_cvt_pk_fp8_f32 rounds every binary32 value in (448, 464] to 448 (0x7E)
+// under round-to-nearest-even (checked on gfx950 for all of them, both signs).
+template <bool SLOW>
+__device__ __forceinline__ uint32_t quant4_path(uint32_t x01, uint32_t x23, const GroupScale& g) {
+  const uint32_t m01 = x01 & 0x7FFF7FFFu, m23 = x23 & 0x7FFF7FFFu;
+  const float a[4] = {bf16_lo(m01), bf16_hi(m01), bf16_lo(m23), bf16_hi(m23)};
+  float qv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float ai = SLOW ? a[i] * kTinyScale : a[i];
+    const float q0 = ai * g.r;
+    const float e = __builtin_fmaf(-q0, g.d, ai);
+    qv[i] = __builtin_fmaf(e, g.r, q0);
   }
-  return __builtin_fminf(q, kE4M3Max);
+  int d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+  d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], d, true);
+  // sign bits: byte 1 and byte 3 of each bf16 pair carry them in bit 7
+  const uint32_t hi_bytes = __builtin_amdgcn_perm(x23, x01, 0x07050301u);
+  return (uint32_t)d | (hi_bytes & 0x80808080u);
 }
 
-// Quantize four bf16 values (two dwords, element 0 in the low half of x01)
-// into four E4M3 codes packed little-endian in one dword.
 __device__ __forceinline__ uint32_t quant4(uint32_t x01, uint32_t x23, const GroupScale& g) {
-  uint32_t m01 = x01 & 0x7FFF7FFFu, m23 = x23 & 0x7FFF7FFFu;
-  float q0 = scaled_mag(bf16_lo(m01), g);
-  float q1 = scaled_mag(bf16_hi(m01), g);
-  float q2 = scaled_mag(bf16_lo(m23), g);
-  float q3 = scaled_mag(bf16_hi(m23), g);
-  int d = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-  d = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, d, true);
-  // sign bits: byte 1 and byte 3 of each bf16 pair carry them in bit 7
-  uint32_t hi_bytes = __builtin_amdgcn_perm(x23, x01, 0x07050301u);
-  return (uint32_t)d | (hi_bytes & 0x80808080u);
+  return g.slow ? quant4_path<true>(x01, x23, g) : quant4_path<false>(x01, x23, g);
+}
+
+// Codes of 2*N bf16 values held in N dwords (in order) -> N/2 code dwords.
+// One branch on the group's path for the whole run.
+template <int N>
+__device__ __forceinline__ void quant_run(const uint32_t* in, uint32_t* out, const GroupScale& g) {
+  static_assert(N % 2 == 0, "pairs of dwords");
+  if (g.slow) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) out[i] = quant4_path<true>(in[2 * i], in[2 * i + 1], g);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) out[i] = quant4_path<false>(in[2 * i], in[2 * i + 1], g);
+  }
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs)

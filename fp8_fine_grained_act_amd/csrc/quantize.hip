@@ -32,16 +32,15 @@ __global__ __launch_bounds__(256) void quant_act_rows_kernel(
   uint4 v0 = src[0];
   uint4 v1 = src[1];
 
-  uint32_t m = max(max(absmax_pair(v0.x), absmax_pair(v0.y)), max(absmax_pair(v0.z), absmax_pair(v0.w)));
-  m = max(m, max(max(absmax_pair(v1.x), absmax_pair(v1.y)), max(absmax_pair(v1.z), absmax_pair(v1.w))));
-  m = max8_u32(m);
+  constexpr uint32_t kMag = 0x7FFF7FFFu;
+  const uint32_t m2 = max_u16x2(max_u16x2(max_u16x2(v0.x & kMag, v0.y & kMag), max_u16x2(v0.z & kMag, v0.w & kMag)),
+                                max_u16x2(max_u16x2(v1.x & kMag, v1.y & kMag), max_u16x2(v1.z & kMag, v1.w & kMag)));
+  const uint32_t m = max8_u32(max(m2 & 0xFFFFu, m2 >> 16));
   GroupScale g = group_scale(m);
 
+  const uint32_t in[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   uint4 out;
-  out.x = quant4(v0.x, v0.y, g);
-  out.y = quant4(v0.z, v0.w, g);
-  out.z = quant4(v1.x, v1.y, g);
-  out.w = quant4(v1.z, v1.w, g);
+  quant_run<8>(in, reinterpret_cast<uint32_t*>(&out), g);
   if (valid) {
     *reinterpret_cast<uint4*>(q + row * ldq + tb * kGroup + lane8 * 16) = out;
     if (lane8 == 0) scales[t] = g.s;
@@ -49,69 +48,157 @@ __global__ __launch_bounds__(256) void quant_act_rows_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Transposed 1x128 tiles (tiles along the rows of x): x [T, C] -> q [C, T],
-// s [C, T/128].  One block handles 128 rows x 64 columns: the bf16 tile is
-// staged through LDS, then each lane owns one column and each wave a quarter
-// (32 rows) of the 128-row group; the four partial amax values meet in LDS.
+// Tiles along the rows (transposed output), optionally fused with the tiles
+// along the columns.  x [T, C] -> qt [C, T], st [C, T/128]; with ROWS also
+// q [T, C], s [T, C/128] from the same read of x.
+//
+// A 256-thread block owns a strip of 128 columns and walks kQGroups squares
+// of 128 x 128 down it.  Each square (32 KB of bf16) is loaded with 8 loads of
+// 16 bytes per thread (every row segment a full 256 bytes) and staged in LDS;
+// the loads of the next square are issued before the current one is coded.
+//
+// LDS: row R of the square is 256 bytes; its 16-byte chunk q sits at chunk
+// q ^ f(R), f(R) = (R & 15) ^ (((R >> 5) & 3) << 2).
+//
+// Transposed tiles use ds_read_b64_tr_b16 (gfx950): in a group of 16 lanes
+// that each point at 4 bf16 of some row, lane i receives element (i mod 4) of
+// the rows addressed by lanes (i div 4), 4 + (i div 4), 8 + (i div 4) and
+// 12 + (i div 4).  Lane j of a group addresses row 32 (j mod 4) + 4t + (j div 4)
+// at a fixed 4-column quad, so after t = 0..7 lane i holds column
+// (quad + i mod 4) for the 32 consecutive rows 32 (i div 4) .. +31.  Those 16
+// rows fall in 16 distinct swizzled chunks (no bank conflict); the four lanes
+// of a column meet through two DPP row rotations for the amax, and each
+// writes its 32 codes as two 16-byte stores.  Each 16-lane group codes two
+// column quads.
+//
+// Row tiles (ROWS) read whole rows with ds_read_b128: a group of 16 lanes is
+// 16 consecutive rows (distinct f(R), no conflict), each lane half a row;
+// the other half sits 16 lanes away.
 // ---------------------------------------------------------------------------
+constexpr int kQB = 128;                   // rows and columns per square
+
+#ifndef FP8BS_QGROUPS
+#define FP8BS_QGROUPS 1
+#endif
+#ifndef FP8BS_QORDER
+#define FP8BS_QORDER 0
+#endif
+constexpr int kQGroups = FP8BS_QGROUPS;    // squares per block, walked down the strip
+constexpr int kQOrder = FP8BS_QORDER;      // 0: blockIdx.x walks column strips, 1: row ranges
+
+__device__ __forceinline__ int qswz(int row) { return (row & 15) ^ (((row >> 5) & 3) << 2); }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+template <bool ROWS>
 __global__ __launch_bounds__(256) void quant_act_cols_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, int64_t cols, uint8_t* __restrict__ q,
-    int64_t ldq, float* __restrict__ scales, int64_t groups_t) {
-  __shared__ uint16_t tile[128][64 + 8];     // +8 bf16 keeps 16-byte row alignment
-  __shared__ uint32_t part[4][64];
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t rows, int64_t cols,
+    uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kQB * 256];
 
   const int tid = threadIdx.x;
-  const int64_t gt = blockIdx.y;             // token group (128 rows)
-  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int64_t rblk = kQOrder ? blockIdx.x : blockIdx.y;
+  const int64_t c0 = (int64_t)(kQOrder ? blockIdx.y : blockIdx.x) * kQB;
+  const int64_t first = rblk * kQGroups * kQB;                 // rows % 128 == 0: squares are full
+  const int nsq = (int)min<int64_t>(kQGroups, (rows - first) / kQB);
 
-  // load 128 rows x 64 columns: 8 lanes x 16 bytes per row, 32 rows per pass
-  {
-    const int chunk = tid & 7;
-    const int r0 = tid >> 3;
-    const int64_t col = c0 + chunk * 8;
-    const bool cok = col < cols;             // cols % 8 == 0, so a chunk is all in or all out
+  // staging lanes: thread (chunk, rr) covers rows rr, rr+16, ... at 16-byte chunk `chunk`.
+  // A chunk past the last column (cols % 8 == 0, so chunks are whole) loads a valid
+  // address of the same row and is replaced by zeros.
+  const int chunk = tid & 15;
+  const int rr = tid >> 4;
+  const bool cok = c0 + chunk * 8 < cols;
+  const uint16_t* src = x + (first + rr) * ldx + (cok ? c0 + chunk * 8 : 0);
+  uint4 v[8];
+  auto load = [&](int sq) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = r0 + 32 * p;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (cok) v = *reinterpret_cast<const uint4*>(x + (gt * 128 + r) * ldx + col);
-      *reinterpret_cast<uint4*>(&tile[r][chunk * 8]) = v;
+    for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(src + ((int64_t)sq * kQB + 16 * i) * ldx);
+    if (!cok) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  load(0);
+
+  const int lane = tid & 15;                                   // lane inside its 16-lane group
+  const int grp16 = tid >> 4;                                  // 16 groups
+  for (int sq = 0; sq < nsq; ++sq) {
+    const int64_t r0 = first + (int64_t)sq * kQB;
+    if (sq) __syncthreads();                                   // the previous square's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = rr + 16 * i;
+      *reinterpret_cast<uint4*>(&tile[row * 256 + ((chunk ^ qswz(row)) << 4)]) = v[i];
+    }
+    __syncthreads();
+    if (sq + 1 < nsq) load(sq + 1);                            // in flight while this square is coded
+
+    // ---- transposed tiles: two column quads per 16-lane group
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cq = grp16 + 16 * u;                           // column quad 0..31
+      const int qc = cq >> 1, half = (cq & 1) << 3;
+      uint32_t vals[16];
+      uint32_t m2 = 0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int row = 32 * (lane & 3) + 4 * t + (lane >> 2);
+        const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(&tile[row * 256 + ((qc ^ qswz(row)) << 4) + half]));
+        vals[2 * t] = (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
+        vals[2 * t + 1] = (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16);
+        m2 = max_u16x2(m2, max_u16x2(vals[2 * t] & 0x7FFF7FFFu, vals[2 * t + 1] & 0x7FFF7FFFu));
+      }
+      uint32_t m = max(m2 & 0xFFFFu, m2 >> 16);
+      m = max(m, dpp_shuffle<0x124>(m));                       // row_ror:4
+      m = max(m, dpp_shuffle<0x128>(m));                       // row_ror:8
+      const int64_t col = c0 + 4 * cq + (lane & 3);
+      if (col < cols) {
+        const GroupScale gs = group_scale(m);
+        uint8_t* dst = qt + col * ldqt + r0 + 32 * (lane >> 2);
+        uint4 o[2];
+        quant_run<16>(vals, reinterpret_cast<uint32_t*>(o), gs);
+        reinterpret_cast<uint4*>(dst)[0] = o[0];
+        reinterpret_cast<uint4*>(dst)[1] = o[1];
+        if ((lane >> 2) == 0) st[col * (rows / kGroup) + r0 / kGroup] = gs.s;
+      }
+    }
+
+    // ---- row tiles (fused mode, cols % 128 == 0): 16 consecutive rows per group, half a row per lane
+    if (ROWS) {
+      const int hh = (tid >> 4) & 1;
+      const int r = lane + 16 * (tid >> 5);
+      uint4 w[8];
+      uint32_t m2 = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        w[j] = *reinterpret_cast<const uint4*>(&tile[r * 256 + (((8 * hh + j) ^ qswz(r)) << 4)]);
+        m2 = max_u16x2(m2, max_u16x2(max_u16x2(w[j].x & 0x7FFF7FFFu, w[j].y & 0x7FFF7FFFu),
+                                     max_u16x2(w[j].z & 0x7FFF7FFFu, w[j].w & 0x7FFF7FFFu)));
+      }
+      uint32_t m = max(m2 & 0xFFFFu, m2 >> 16);
+      m = max(m, (uint32_t)__shfl_xor((int)m, 16));            // the other half of the row
+      const GroupScale gs = group_scale(m);
+      uint8_t* dst = q + (r0 + r) * ldq + c0 + 64 * hh;
+      uint4 o[4];
+      quant_run<32>(reinterpret_cast<const uint32_t*>(w), reinterpret_cast<uint32_t*>(o), gs);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) reinterpret_cast<uint4*>(dst)[j] = o[j];
+      if (hh == 0) s[(r0 + r) * (cols / kGroup) + c0 / kGroup] = gs.s;
     }
   }
-  __syncthreads();
+}
 
-  const int lane = tid & 63;
-  const int wave = tid >> 6;                 // rows 32*wave .. 32*wave+31
-  uint32_t vals[16];                         // 32 bf16, packed in pairs along the rows
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint32_t lo = tile[32 * wave + 2 * i][lane];
-    uint32_t hi = tile[32 * wave + 2 * i + 1][lane];
-    vals[i] = lo | (hi << 16);
-    m = max(m, absmax_pair(vals[i]));
-  }
-  part[wave][lane] = m;
-  __syncthreads();
-  m = max(max(part[0][lane], part[1][lane]), max(part[2][lane], part[3][lane]));
-  GroupScale g = group_scale(m);
-
-  const int64_t col = c0 + lane;
-  if (col < cols) {
-    uint8_t* dst = q + col * ldq + gt * 128 + 32 * wave;
-    uint4 o0, o1;
-    o0.x = quant4(vals[0], vals[1], g);
-    o0.y = quant4(vals[2], vals[3], g);
-    o0.z = quant4(vals[4], vals[5], g);
-    o0.w = quant4(vals[6], vals[7], g);
-    o1.x = quant4(vals[8], vals[9], g);
-    o1.y = quant4(vals[10], vals[11], g);
-    o1.z = quant4(vals[12], vals[13], g);
-    o1.w = quant4(vals[14], vals[15], g);
-    reinterpret_cast<uint4*>(dst)[0] = o0;
-    reinterpret_cast<uint4*>(dst)[1] = o1;
-    if (wave == 0) scales[col * groups_t + gt] = g.s;
-  }
+static dim3 cols_grid(int64_t rows, int64_t cols) {
+  const int64_t rb = (rows / kQB + kQGroups - 1) / kQGroups;
+  const int64_t cb = (cols + kQB - 1) / kQB;
+  return kQOrder ? dim3((unsigned)rb, (unsigned)cb) : dim3((unsigned)cb, (unsigned)rb);
+}
+static bool cols_grid_ok(int64_t rows, int64_t cols) {
+  const int64_t rb = (rows / kQB + kQGroups - 1) / kQGroups;
+  const int64_t cb = (cols + kQB - 1) / kQB;
+  return kQOrder ? (cb <= 65535 && rb <= kMaxGrid) : (rb <= 65535 && cb <= kMaxGrid);
 }
 
 // ---------------------------------------------------------------------------
@@ -136,24 +223,22 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(base + (int64_t)(16 * i) * ldw);
 
-  uint32_t m = 0;
+  constexpr uint32_t kMag = 0x7FFF7FFFu;
+  uint32_t m2 = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    m = max(m, max(max(absmax_pair(v[i].x), absmax_pair(v[i].y)), max(absmax_pair(v[i].z), absmax_pair(v[i].w))));
-  m = wave_max_u32(m);
+    m2 = max_u16x2(m2, max_u16x2(max_u16x2(v[i].x & kMag, v[i].y & kMag), max_u16x2(v[i].z & kMag, v[i].w & kMag)));
+  uint32_t m = wave_max_u32(max(m2 & 0xFFFFu, m2 >> 16));
   if ((tid & 63) == 0) part[tid >> 6] = m;
   __syncthreads();
   m = max(max(part[0], part[1]), max(part[2], part[3]));
   GroupScale g = group_scale(m);
 
   uint8_t* dst = q + (bn * 128 + rr) * ldq + bk * 128 + chunk * 8;
+  uint2 o[8];
+  quant_run<32>(reinterpret_cast<const uint32_t*>(v), reinterpret_cast<uint32_t*>(o), g);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint2 o;
-    o.x = quant4(v[i].x, v[i].y, g);
-    o.y = quant4(v[i].z, v[i].w, g);
-    *reinterpret_cast<uint2*>(dst + (int64_t)(16 * i) * ldq) = o;
-  }
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint2*>(dst + (int64_t)(16 * i) * ldq) = o[i];
   if (tid == 0) scales[blk] = g.s;
 }
 
@@ -181,12 +266,25 @@ extern "C" int fp8bs_quantize_act_1x128(const uint16_t* x, int64_t rows, int64_t
                        ldq, scales, tpr, total);
   } else {
     if (rows % kGroup || cols % 8 || ldq < rows) return FP8BS_ERR_SHAPE;
-    const int64_t gt = rows / kGroup;
-    const int64_t cb = (cols + 63) / 64;
-    if (gt > 65535 || cb > kMaxGrid) return FP8BS_ERR_SHAPE;
-    hipLaunchKernelGGL(quant_act_cols_kernel, dim3((unsigned)cb, (unsigned)gt), dim3(256), 0, s, x,
-                       ldx, cols, q, ldq, scales, gt);
+    if (!cols_grid_ok(rows, cols)) return FP8BS_ERR_SHAPE;
+    hipLaunchKernelGGL(quant_act_cols_kernel<false>, cols_grid(rows, cols), dim3(256), 0, s, x,
+                       ldx, rows, cols, q, ldq, scales, (uint8_t*)nullptr, (int64_t)0, (float*)nullptr);
   }
+  return launch_status();
+}
+
+extern "C" int fp8bs_quantize_act_1x128_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                             uint8_t* q, int64_t ldq, float* scales, uint8_t* qt,
+                                             int64_t ldqt, float* scales_t, void* stream) {
+  if (!x || !q || !scales || !qt || !scales_t) return FP8BS_ERR_NULL;
+  if (rows <= 0 || cols <= 0 || rows % kGroup || cols % kGroup) return FP8BS_ERR_SHAPE;
+  if (ldx < cols || ldq < cols || ldqt < rows) return FP8BS_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(qt, 16) || !aligned(scales, 4) ||
+      !aligned(scales_t, 4) || ldx % 8 || ldq % 16 || ldqt % 16)
+    return FP8BS_ERR_ALIGN;
+  if (!cols_grid_ok(rows, cols)) return FP8BS_ERR_SHAPE;
+  hipLaunchKernelGGL(quant_act_cols_kernel<true>, cols_grid(rows, cols), dim3(256), 0,
+                     (hipStream_t)stream, x, ldx, rows, cols, qt, ldqt, scales_t, q, ldq, scales);
   return launch_status();
 }
 

@@ -22,6 +22,8 @@ _c_void_p, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 
 _SIGNATURES = {
     "fp8bs_quantize_act_1x128": [_c_void_p, _i64, _i64, _i64, _int, _c_void_p, _i64, _c_void_p, _c_void_p],
+    "fp8bs_quantize_act_1x128_dual": [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _i64,
+                                      _c_void_p, _c_void_p],
     "fp8bs_quantize_w_128x128": [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p],
     "fp8bs_gemm": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int, _c_void_p, _i64,
                    _c_void_p],
@@ -112,6 +114,34 @@ def fp8bs_quantize_act_1x128(x, transpose=0, q=None, scales=None, stream=None):
                                       scales.data_ptr(), _stream(stream))
     _check("fp8bs_quantize_act_1x128", st)
     return q, scales
+
+
+def fp8bs_quantize_act_1x128_dual(x, q=None, scales=None, qt=None, scales_t=None, stream=None):
+    """Both 1x128 orientations of bf16 x [rows, cols] from one read.
+
+    Returns (q [rows, cols], scales [rows, cols/128], qt [cols, rows], scales_t [cols, rows/128]),
+    bit-identical to fp8bs_quantize_act_1x128 with transpose=0 and transpose=1.
+    """
+    _dev(x, torch.bfloat16, "x")
+    ldx = _row_major(x, "x")
+    rows, cols = x.shape
+    mk = lambda t, shape, dt: torch.empty(shape, dtype=dt, device=x.device) if t is None else t  # noqa: E731
+    q = mk(q, (rows, cols), torch.uint8)
+    scales = mk(scales, (rows, cols // GROUP), torch.float32)
+    qt = mk(qt, (cols, rows), torch.uint8)
+    scales_t = mk(scales_t, (cols, rows // GROUP), torch.float32)
+    for t, dt, name in ((q, torch.uint8, "q"), (scales, torch.float32, "scales"), (qt, torch.uint8, "qt"),
+                        (scales_t, torch.float32, "scales_t")):
+        _dev(t, dt, name)
+    ldq, ldqt = _row_major(q, "q"), _row_major(qt, "qt")
+    if (tuple(q.shape) != (rows, cols) or tuple(qt.shape) != (cols, rows)
+            or tuple(scales.shape) != (rows, cols // GROUP) or tuple(scales_t.shape) != (cols, rows // GROUP)
+            or not scales.is_contiguous() or not scales_t.is_contiguous()):
+        raise ValueError("output shapes do not match the input")
+    st = raw.fp8bs_quantize_act_1x128_dual(x.data_ptr(), rows, cols, ldx, q.data_ptr(), ldq, scales.data_ptr(),
+                                           qt.data_ptr(), ldqt, scales_t.data_ptr(), _stream(stream))
+    _check("fp8bs_quantize_act_1x128_dual", st)
+    return q, scales, qt, scales_t
 
 
 def fp8bs_quantize_w_128x128(w, q=None, scales=None, stream=None):

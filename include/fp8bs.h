@@ -79,6 +79,26 @@ int fp8bs_quantize_act_1x128(const uint16_t* x, int64_t rows, int64_t cols, int6
                              void* stream);
 
 /*
+ * Both orientations of the 1x128 activation tiles from one read of x.
+ * In a training step an activation (and its output gradient) is the FP8
+ * input of two GEMMs with different contractions ("DeepSeek-V3 技术报告深度解读",
+ * section 3: forward / activation gradient contract over the columns, the
+ * weight gradient over the tokens), so it is quantized along both.  The
+ * outputs are bit-identical to fp8bs_quantize_act_1x128 with transpose == 0
+ * (q, scales) and with transpose == 1 (qt, scales_t); x is read once.
+ *   x         bf16 [rows, cols], row stride ldx elements
+ *   q         E4M3 [rows, cols], row stride ldq bytes;   scales   f32 [rows, cols/128]
+ *   qt        E4M3 [cols, rows], row stride ldqt bytes;  scales_t f32 [cols, rows/128]
+ *   rows % 128 == 0, cols % 128 == 0.
+ * Alignment: x, q, qt 16-byte aligned, ldx % 8 == 0, ldq % 16 == 0,
+ * ldqt % 16 == 0, scales and scales_t 4-byte aligned.  The four outputs must
+ * not overlap each other or x.
+ */
+int fp8bs_quantize_act_1x128_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* scales, uint8_t* qt,
+                                  int64_t ldqt, float* scales_t, void* stream);
+
+/*
  * Weight quantization in 128x128 blocks (the pages' weight granularity).
  *   w       bf16 [n, k], row stride ldw elements
  *   q       E4M3 [n, k], row stride ldq bytes

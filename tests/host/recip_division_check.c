@@ -1,13 +1,17 @@
 /*
- * Host check of the quantizer's division identity (used by the HIP kernels):
- * for every pair of positive bf16 values (amax, x) with x <= amax and
- * amax >= 2^-64 (tiles below that use IEEE division), with s = fl32(amax/448)
- * and r = fl32(1/s), the correction step
- *     q0 = x*r;  e = fma(-q0, s, x);  q = fma(e, r, q0)
- * must give the same E4M3 code (round to nearest even, saturating at 448) as
- * the IEEE binary32 quotient x/s.  Negative x is covered by symmetry: the
- * kernels quantize |x| and restore the sign bit afterwards.
- * Exit status 0 when every pair agrees; prints the counts.
+ * Host check of the quantizer's division identity (used by the HIP kernels).
+ * For every pair of non-negative bf16 values (amax, x) with x <= amax and
+ * s = fl32(amax/448):
+ *   amax >= threshold (2^-64 in the kernels): d = s, r = fl32(1/d), a = x;
+ *   amax <  threshold (tiny tiles):           d = s * 2^64, r = fl32(1/d)
+ *                                             (0 when d == 0), a = x * 2^64;
+ * the correction step
+ *     q0 = a*r;  e = fma(-q0, d, a);  q = fma(e, r, q0)
+ * must give the same E4M3 code (round to nearest even, saturating) as the
+ * IEEE binary32 quotient x/s, and q must not exceed 464 (the hardware
+ * conversion rounds (448, 464] to 448; above that it would not saturate).
+ * Negative x is covered by symmetry: the kernels quantize |x| and restore the
+ * sign bit afterwards.  Exit status 0 when every pair agrees; prints counts.
  */
 #include <math.h>
 #include <stdint.h>
@@ -35,27 +39,36 @@ static uint32_t e4m3(float v) {
   return c > 0x7E ? 0x7E : (uint32_t)c;
 }
 
-int main(int argc, char** argv) {
-  uint32_t tiny_bits = argc > 1 ? (uint32_t)strtoul(argv[1], 0, 0) : 0x1F80u;
-  long long pairs = 0, bad = 0;
-  for (uint32_t ab = tiny_bits; ab < 0x7F80; ++ab) {
+static long long check_range(uint32_t lo, uint32_t hi, int tiny, long long* pairs) {
+  long long bad = 0;
+  for (uint32_t ab = lo; ab < hi; ++ab) {
     float amax = from_bf16(ab);
     float s = amax / 448.0f;
-    float r = 1.0f / s;
+    float d = tiny ? s * 0x1p64f : s;
+    float r = d == 0.0f ? 0.0f : 1.0f / d;
     for (uint32_t xb = 0; xb <= ab; ++xb) {
       float x = from_bf16(xb);
-      float q0 = x * r;
-      float e = fmaf(-q0, s, x);
+      float a = tiny ? x * 0x1p64f : x;
+      float q0 = a * r;
+      float e = fmaf(-q0, d, a);
       float q = fmaf(e, r, q0);
-      if (q > 448.0f) q = 448.0f;
-      float ref = x / s;
-      ++pairs;
-      if (e4m3(q) != e4m3(ref)) {
+      float ref = s == 0.0f ? 0.0f : x / s;
+      ++*pairs;
+      if (e4m3(q) != e4m3(ref) || q > 464.0f) {
         if (bad < 5) printf("mismatch amax=%a x=%a q=%a ieee=%a\n", amax, x, q, ref);
         ++bad;
       }
     }
   }
+  return bad;
+}
+
+int main(int argc, char** argv) {
+  uint32_t tiny_bits = argc > 1 ? (uint32_t)strtoul(argv[1], 0, 0) : 0x1F80u;
+  long long pairs_tiny = 0, pairs = 0;
+  long long bad_tiny = check_range(0, tiny_bits, 1, &pairs_tiny);
+  long long bad = check_range(tiny_bits, 0x7F80, 0, &pairs);
+  printf("tiny: pairs=%lld mismatches=%lld (amax < bf16 0x%04x, scaled by 2^64)\n", pairs_tiny, bad_tiny, tiny_bits);
   printf("pairs=%lld mismatches=%lld (amax >= bf16 0x%04x)\n", pairs, bad, tiny_bits);
-  return bad != 0;
+  return (bad != 0 || bad_tiny != 0);
 }

@@ -65,6 +65,20 @@ def test_quantize_act_validation(raw):
     assert f(P, 128, 64, 64, 1, P, 64, P, None) == ESHAPE           # transposed: ldq < rows
 
 
+def test_quantize_act_dual_validation(raw):
+    f = raw.fp8bs_quantize_act_1x128_dual
+    assert f(P, 128, 128, 128, P, 128, P, None, 128, P, None) == ENULL
+    assert f(P, 100, 128, 128, P, 128, P, P, 112, P, None) == ESHAPE   # rows % 128
+    assert f(P, 128, 64, 64, P, 64, P, P, 128, P, None) == ESHAPE      # cols % 128
+    assert f(P, 0, 128, 128, P, 128, P, P, 128, P, None) == ESHAPE
+    assert f(P, 128, 128, 64, P, 128, P, P, 128, P, None) == ESHAPE    # ldx < cols
+    assert f(P, 256, 128, 128, P, 128, P, P, 128, P, None) == ESHAPE   # ldqt < rows
+    assert f(P, 128, 128, 132, P, 128, P, P, 128, P, None) == EALIGN   # ldx % 8
+    assert f(P_ODD, 128, 128, 128, P, 128, P, P, 128, P, None) == EALIGN
+    assert f(P, 128, 128, 128, P, 136, P, P, 128, P, None) == EALIGN   # ldq % 16
+    assert f(P, 128, 128, 128, P, 128, P, P, 136, P, None) == EALIGN   # ldqt % 16
+
+
 def test_quantize_w_validation(raw):
     f = raw.fp8bs_quantize_w_128x128
     assert f(P, 128, 128, 128, None, 128, P, None) == ENULL

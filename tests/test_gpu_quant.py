@@ -163,6 +163,61 @@ def test_act_transposed_c5(gpu_lib):
         _assert_same(f"c5 {key}^T", q[cols], s[cols], q_ref, s_ref)
 
 
+def _dual(lib, bits):
+    q, s, qt, st = lib.fp8bs_quantize_act_1x128_dual(to_dev_bf16(bits))
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy(), qt.cpu().numpy(), st.cpu().numpy()
+
+
+def test_act_dual_small_and_edges(gpu_lib):
+    rng = np.random.default_rng(106)
+    for t, c in [(128, 128), (384, 256), (256, 1024), (640, 384), (128, 7168)]:
+        bits = _edge_matrix(rng, t, c)
+        # an edge column too: all -0 in one 128-token group, subnormals in another
+        bits[:128, 5] = 0x8000
+        if t > 128:
+            bits[128:256, 9] = rng.integers(0x0001, 0x0080, size=128)
+        q, s, qt, st = _dual(gpu_lib, bits)
+        _assert_same(f"dual rows {t}x{c}", q, s, *quantize_act_1x128(bits))
+        _assert_same(f"dual transposed {t}x{c}", qt, st, *quantize_act_1x128_t(bits))
+
+
+@pytest.mark.parametrize("name,key", [("c2", "a"), ("c2", "dy"), ("c5", "dy")])
+def test_act_dual_configs(gpu_lib, name, key):
+    from workloads import layer_inputs
+
+    bits = (layer_inputs(name) if name == "c2" else wgrad_inputs(name))[key]
+    q, s, qt, st = _dual(gpu_lib, bits)
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(bits.shape[0], 192, replace=False))
+    _assert_same(f"{name} {key} dual rows", q[rows], s[rows], *quantize_act_1x128(bits[rows]))
+    cols = np.sort(rng.choice(bits.shape[1], 64, replace=False))
+    q_ref, s_ref = quantize_act_1x128_t(np.ascontiguousarray(bits[:, cols]))
+    _assert_same(f"{name} {key} dual transposed", qt[cols], st[cols], q_ref, s_ref)
+    # the two orientations equal the single-orientation entry point bit for bit
+    q1, s1 = _act(gpu_lib, bits, transpose=0)
+    q2, s2 = _act(gpu_lib, bits, transpose=1)
+    assert np.array_equal(q, q1) and np.array_equal(s.view(np.uint32), s1.view(np.uint32))
+    assert np.array_equal(qt, q2) and np.array_equal(st.view(np.uint32), s2.view(np.uint32))
+
+
+def test_act_dual_strided_buffers(gpu_lib):
+    rng = np.random.default_rng(107)
+    full = f32_to_bf16_bits(rng.standard_normal((384, 520)).astype(np.float32))
+    x = to_dev_bf16(full)[:, 8:520]                                   # ldx = 520, cols = 512
+    q = torch.full((384, 528), 0xAB, dtype=torch.uint8, device="cuda")[:, :512]
+    qt = torch.full((512, 400), 0xCD, dtype=torch.uint8, device="cuda")[:, :384]
+    s = torch.empty((384, 4), dtype=torch.float32, device="cuda")
+    st = torch.empty((512, 3), dtype=torch.float32, device="cuda")
+    gpu_lib.fp8bs_quantize_act_1x128_dual(x, q=q, scales=s, qt=qt, scales_t=st)
+    torch.cuda.synchronize()
+    sub = np.ascontiguousarray(full[:, 8:520])
+    _assert_same("dual strided rows", q.cpu().numpy(), s.cpu().numpy(), *quantize_act_1x128(sub))
+    _assert_same("dual strided transposed", qt.cpu().numpy(), st.cpu().numpy(), *quantize_act_1x128_t(sub))
+    assert np.all(q.as_strided((384, 528), (528, 1)).cpu().numpy()[:, 512:] == 0xAB)
+    assert np.all(qt.as_strided((512, 400), (400, 1)).cpu().numpy()[:, 384:] == 0xCD)
+
+
 def test_weight_blocks_small_and_edges(gpu_lib):
     rng = np.random.default_rng(104)
     for n, k in [(128, 128), (256, 384), (384, 1024)]:
