@@ -53,6 +53,8 @@ def parse_args():
     p.add_argument("--cpu-sample-rows", type=int, default=4096)
     p.add_argument("--kernel-reps", type=int, default=24, help="launches per per-kernel timing graph")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of step graphs")
+    p.add_argument("--separate-quant", action="store_true",
+                   help="quantize each activation orientation with its own call instead of the fused call")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 512 MiB device-to-device copies (reference for HBM byte counters)")
     return p.parse_args()
@@ -80,8 +82,13 @@ class Call:
         self.times_ms = []
 
 
-def build_layer_step(lib, cfg_name, rotate):
-    """Calls of one training pass of a linear layer (configs c2 / c3 shapes)."""
+def build_layer_step(lib, cfg_name, rotate, dual=True):
+    """Calls of one training pass of a linear layer (configs c2 / c3 shapes).
+
+    With ``dual`` (default) X and dY are each quantized once into both
+    orientations (1x128 tiles along the features for forward / dgrad, along
+    the tokens for wgrad); otherwise each orientation is its own call.
+    """
     import torch
 
     from workloads import config_by_name, layer_inputs
@@ -110,29 +117,50 @@ def build_layer_step(lib, cfg_name, rotate):
         return sets[state["i"] % rotate]
 
     act_bytes = lambda r, c: r * c * 3 + r * c // 128 * 4  # noqa: E731
-    calls = [
-        Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(cur()[0], q=qx, scales=sx),
-             nbytes=act_bytes(m, k), outs=(qx, sx)),
-        Call("quant_w", "quant", lambda: lib.fp8bs_quantize_w_128x128(cur()[1], q=qw, scales=sw),
-             nbytes=n * k * 3 + (n // 128) * (k // 128) * 4, outs=(qw, sw)),
-        Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k,
-             outs=(y,)),
-        Call("quant_act_dy", "quant", lambda: lib.fp8bs_quantize_act_1x128(cur()[2], q=qdy, scales=sdy),
-             nbytes=act_bytes(m, n), outs=(qdy, sdy)),
-        Call("gemm_dgrad", "gemm", lambda: lib.fp8bs_gemm(qdy, sdy, qw, sw, b_layout=1, c=dx),
-             flops=2.0 * m * n * k, outs=(dx,)),
-        Call("quant_act_dy_t", "quant",
-             lambda: lib.fp8bs_quantize_act_1x128(cur()[2], transpose=1, q=qdyt, scales=sdyt),
-             nbytes=act_bytes(m, n), outs=(qdyt, sdyt)),
-        Call("quant_act_x_t", "quant",
-             lambda: lib.fp8bs_quantize_act_1x128(cur()[0], transpose=1, q=qxt, scales=sxt),
-             nbytes=act_bytes(m, k), outs=(qxt, sxt)),
-        Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdyt, sdyt, qxt, sxt, c=dw),
-             flops=2.0 * m * n * k, outs=(dw,)),
-    ]
+    dual_bytes = lambda r, c: r * c * 4 + 2 * (r * c // 128) * 4  # noqa: E731
+    if dual:
+        calls = [
+            Call("quant_act_x_dual", "quant",
+                 lambda: lib.fp8bs_quantize_act_1x128_dual(cur()[0], q=qx, scales=sx, qt=qxt, scales_t=sxt),
+                 nbytes=dual_bytes(m, k), outs=(qx, sx, qxt, sxt)),
+            Call("quant_w", "quant", lambda: lib.fp8bs_quantize_w_128x128(cur()[1], q=qw, scales=sw),
+                 nbytes=n * k * 3 + (n // 128) * (k // 128) * 4, outs=(qw, sw)),
+            Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k,
+                 outs=(y,)),
+            Call("quant_act_dy_dual", "quant",
+                 lambda: lib.fp8bs_quantize_act_1x128_dual(cur()[2], q=qdy, scales=sdy, qt=qdyt, scales_t=sdyt),
+                 nbytes=dual_bytes(m, n), outs=(qdy, sdy, qdyt, sdyt)),
+            Call("gemm_dgrad", "gemm", lambda: lib.fp8bs_gemm(qdy, sdy, qw, sw, b_layout=1, c=dx),
+                 flops=2.0 * m * n * k, outs=(dx,)),
+            Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdyt, sdyt, qxt, sxt, c=dw),
+                 flops=2.0 * m * n * k, outs=(dw,)),
+        ]
+    else:
+        calls = [
+            Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(cur()[0], q=qx, scales=sx),
+                 nbytes=act_bytes(m, k), outs=(qx, sx)),
+            Call("quant_w", "quant", lambda: lib.fp8bs_quantize_w_128x128(cur()[1], q=qw, scales=sw),
+                 nbytes=n * k * 3 + (n // 128) * (k // 128) * 4, outs=(qw, sw)),
+            Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k,
+                 outs=(y,)),
+            Call("quant_act_dy", "quant", lambda: lib.fp8bs_quantize_act_1x128(cur()[2], q=qdy, scales=sdy),
+                 nbytes=act_bytes(m, n), outs=(qdy, sdy)),
+            Call("gemm_dgrad", "gemm", lambda: lib.fp8bs_gemm(qdy, sdy, qw, sw, b_layout=1, c=dx),
+                 flops=2.0 * m * n * k, outs=(dx,)),
+            Call("quant_act_dy_t", "quant",
+                 lambda: lib.fp8bs_quantize_act_1x128(cur()[2], transpose=1, q=qdyt, scales=sdyt),
+                 nbytes=act_bytes(m, n), outs=(qdyt, sdyt)),
+            Call("quant_act_x_t", "quant",
+                 lambda: lib.fp8bs_quantize_act_1x128(cur()[0], transpose=1, q=qxt, scales=sxt),
+                 nbytes=act_bytes(m, k), outs=(qxt, sxt)),
+            Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdyt, sdyt, qxt, sxt, c=dw),
+                 flops=2.0 * m * n * k, outs=(dw,)),
+        ]
     desc = dict(workload=f"{cfg_name}: one FP8 training pass (forward + dgrad + wgrad, all quantization "
                          f"included) of a linear layer, {cfg['desc']}",
-                M_tokens=m, N_out=n, K_in=k, input_copies=rotate)
+                M_tokens=m, N_out=n, K_in=k, input_copies=rotate,
+                activation_quantization="one call per tensor for both orientations" if dual
+                else "one call per tensor and orientation")
     return calls, state, desc, d
 
 
@@ -366,7 +394,7 @@ def main():
         return
 
     if args.config in ("c2", "c3"):
-        calls, state, desc, data = build_layer_step(lib, args.config, args.rotate)
+        calls, state, desc, data = build_layer_step(lib, args.config, args.rotate, dual=not args.separate_quant)
     elif args.config == "c4":
         calls, state, desc, data = build_grouped_step(lib, args.rotate)
     else:

@@ -12,7 +12,12 @@
 // products span many binades); the FP32 promotion bounds how far that error
 // can accumulate, as on the pages' hardware.
 //
-// Structure of one workgroup (WAVES_M x WAVES_N waves, each wave a
+// Two kernels share the slab layout below: gemm_kernel (128 x 128 tiles, every
+// wave both copies and multiplies, two workgroups per CU; also the MoE grouped
+// GEMM) and gemm_ws_kernel (256 x 128 tiles, separate copy and MFMA waves,
+// described above that kernel).
+//
+// Structure of one gemm_kernel workgroup (WAVES_M x WAVES_N waves, each wave a
 // (BM/WAVES_M) x (BN/WAVES_N) patch of 16x16 MFMA tiles):
 //   * K is walked in 128-deep slabs.  A slab of A (BM rows x 128 bytes), of B
 //     and of the scales that go with it is copied from memory straight into
@@ -20,9 +25,6 @@
 //     flight; no VGPRs hold staged data, and rows past the matrix edge read as
 //     zero (buffer range check).  Each stage is its own LDS object, so the
 //     compiler can tell a slab being filled from the slab being read.
-//   * The MFMA operands of slab k+1 are read from LDS into a second register
-//     set while the MFMAs of slab k run (register double buffering), so LDS
-//     latency sits under matrix-core time.
 //   * LDS rows are 128 bytes of 16-byte chunks; chunk c of row r is stored at
 //     chunk c ^ ((r >> 1) & 7).  A 16-lane pass of ds_read_b128 then reads 16
 //     distinct 16-byte bank groups (two rows fill the 64 banks).
@@ -37,6 +39,8 @@
 //     b = 0..7; pointing even lanes at 8 consecutive k rows of columns n..n+7
 //     and odd lanes at the same rows of columns n+8..n+15 leaves lane i with 8
 //     consecutive k of column n + i.
+
+#include <stdlib.h>
 
 #include "common.h"
 #include "launch.h"
@@ -139,7 +143,7 @@ struct GemmCfg {
   }
 };
 
-template <int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool DBUF>
+template <int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void gemm_kernel(GemmArgs p) {
   using C = GemmCfg<MODE, BM, BN, WAVES_M, WAVES_N, STAGES>;
@@ -193,34 +197,31 @@ void gemm_kernel(GemmArgs p) {
   }
 
   // ---- one slab's copies ------------------------------------------------------
-  auto issue_slab = [&](int kb, Stage<BM, BN>& s) {
+  // Copy job q of this wave: q < A_CP an A copy (8 rows, 1 KB), then B_CP B
+  // copies, then at most kScaleRounds scale copies (64 floats each).
+  auto issue_job = [&](int kb, Stage<BM, BN>& s, int q) {
     const uint32_t ks = (uint32_t)kb * BK;
-#pragma unroll
-    for (int i = 0; i < C::A_CP; ++i) {
-      const int j = i * NW + wave;
+    if (q < C::A_CP) {
+      const int j = q * NW + wave;
       const int c = j * 64 + lane, row = c >> 3, pc = c & 7;
       const int lc = pc ^ ((row >> 1) & 7);
       dma16(ra, s.a + j * 1024, (uint32_t)(row * K + (lc << 4)), ks);
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_CP; ++i) {
-      const int j = i * NW + wave;
+    } else if (q < C::A_CP + C::B_CP) {
+      const int j = (q - C::A_CP) * NW + wave;
       const int c = j * 64 + lane, row = c >> 3, pc = c & 7;
       const int lc = pc ^ ((row >> 1) & 7);
       if (MODE == kDgrad)
         dma16(rb, s.b + j * 1024, (uint32_t)(row * N + (lc << 4)), ks * (uint32_t)N);
       else
         dma16(rb, s.b + j * 1024, (uint32_t)(row * K + (lc << 4)), ks);
-    }
-#pragma unroll
-    for (int r = 0; r < C::kScaleRounds; ++r) {
-      const int js = r * NW + wave;
+    } else {
+      const int js = (q - C::A_CP - C::B_CP) * NW + wave;
       if (js < C::kScaleJobs) {
-        const int q = js * 64 + lane;            // scale slot: [0, BM) rows of A, [BM, BM+BN) columns
+        const int qq = js * 64 + lane;           // scale slot: [0, BM) rows of A, [BM, BM+BN) columns
         if (js * 64 < BM) {
-          dma4(rsa, s.sa + js * 64, (uint32_t)(q * nkb) * 4u, (uint32_t)kb * 4u);
+          dma4(rsa, s.sa + js * 64, (uint32_t)(qq * nkb) * 4u, (uint32_t)kb * 4u);
         } else {
-          const int col = q - BM;
+          const int col = qq - BM;
           float* dst = s.sb + (js * 64 - BM);
           if (MODE == kWgrad) {
             dma4(rsb, dst, (uint32_t)(col * nkb) * 4u, (uint32_t)kb * 4u);
@@ -234,6 +235,11 @@ void gemm_kernel(GemmArgs p) {
       }
     }
   };
+  constexpr int kJobs = C::A_CP + C::B_CP + C::kScaleRounds;
+  auto issue_slab = [&](int kb, Stage<BM, BN>& s) {
+#pragma unroll
+    for (int q = 0; q < kJobs; ++q) issue_job(kb, s, q);
+  };
 
   // ---- operand fragments of one slab -----------------------------------------
   struct Frags {
@@ -241,14 +247,15 @@ void gemm_kernel(GemmArgs p) {
     float wa[TM];
     v4f wb[TN];
   };
+  auto read_a = [&](const Stage<BM, BN>& s, int j) -> v8i {
+    const int r = WM * wm + 16 * j + l16;
+    const uint4 lo = *reinterpret_cast<const uint4*>(&s.a[swz(r, 2 * g)]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(&s.a[swz(r, 2 * g + 1)]);
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
   auto load_frags = [&](const Stage<BM, BN>& s, Frags& f) {
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int r = WM * wm + 16 * j + l16;
-      const uint4 lo = *reinterpret_cast<const uint4*>(&s.a[swz(r, 2 * g)]);
-      const uint4 hi = *reinterpret_cast<const uint4*>(&s.a[swz(r, 2 * g + 1)]);
-      f.af[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+    for (int j = 0; j < TM; ++j) f.af[j] = read_a(s, j);
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       if (MODE == kDgrad) {
@@ -289,21 +296,27 @@ void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // acc[i][j] += (sa * sb) * P for one 16x16 tile of this slab
+  auto rescale = [&](const Frags& f, int i, int j, const v4f& P) {
+    if (MODE == kWgrad) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(f.wa[j] * f.wb[i][v], P[v], acc[i][j][v]);
+    } else {
+      const float w = f.wa[j] * f.wb[i][0];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(w, P[v], acc[i][j][v]);
+    }
+  };
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+  // every fragment of the slab in registers, then the MFMAs
   auto mfma_phase = [&](const Frags& f) {
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
         const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.bf[i], f.af[j], zero, 0, 0, 0, 0, 0, 0);
-        if (MODE == kWgrad) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(f.wa[j] * f.wb[i][v], P[v], acc[i][j][v]);
-        } else {
-          const float w = f.wa[j] * f.wb[i][0];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(w, P[v], acc[i][j][v]);
-        }
+        rescale(f, i, j, P);
       }
     }
   };
@@ -331,47 +344,21 @@ void gemm_kernel(GemmArgs p) {
   for (int s = 0; s < STAGES; ++s)
     if (s < nkb) issue_slab(s, stage_ref(s));
 
-  if (DBUF) {
-    // slab kb's fragments sit in fr[kb & 1]; iteration kb reads slab kb+1's into
-    // the other set, refills the stage slab kb lived in with slab kb+STAGES,
-    // then runs slab kb's MFMAs (LDS latency under matrix-core time)
-    Frags fr[2];
-    publish(min(STAGES - 1, nkb - 1));
-    load_frags(stage_ref(0), fr[0]);
-    for (int kb0 = 0; kb0 < nkb; kb0 += 2 * STAGES) {
+  // publish slab kb, read its fragments, refill the stage of slab kb-1 (read
+  // by every wave before this barrier), run slab kb's MFMAs
+  for (int kb0 = 0; kb0 < nkb; kb0 += STAGES) {
 #pragma unroll
-      for (int u = 0; u < 2 * STAGES; ++u) {
-        const int kb = kb0 + u;
-        if (kb < nkb) {
-          const int s_cur = u % STAGES, s_nxt = (u + 1) % STAGES;
-          if (kb + 1 < nkb) {
-            publish(min(STAGES - 2, nkb - kb - 2));
-            load_frags(stage_ref(s_nxt), fr[(u + 1) & 1]);
-          }
-          // every wave passed the barrier above after reading slab kb's
-          // fragments, so stage s_cur is free
-          if (kb + STAGES < nkb) issue_slab(kb + STAGES, stage_ref(s_cur));
-          mfma_phase(fr[u & 1]);
-        }
-      }
-    }
-  } else {
-    // single fragment set: publish slab kb, read its fragments, refill the
-    // stage of slab kb-1 (read by every wave before this barrier), run MFMAs
-    for (int kb0 = 0; kb0 < nkb; kb0 += STAGES) {
-#pragma unroll
-      for (int u = 0; u < STAGES; ++u) {
-        const int kb = kb0 + u;
-        if (kb < nkb) {
-          // slabs issued so far: 0 .. STAGES-1 (prologue) and kb-2+STAGES
-          // (refills), so slab kb has min(STAGES-1 (first) or STAGES-2, rest)
-          // newer copies behind it
-          publish(kb == 0 ? min(STAGES - 1, nkb - 1) : min(STAGES - 2, nkb - kb - 1));
-          Frags f;
-          load_frags(stage_ref(u), f);
-          if (kb >= 1 && kb - 1 + STAGES < nkb) issue_slab(kb - 1 + STAGES, stage_ref((u + STAGES - 1) % STAGES));
-          mfma_phase(f);
-        }
+    for (int u = 0; u < STAGES; ++u) {
+      const int kb = kb0 + u;
+      if (kb < nkb) {
+        // slabs issued so far: 0 .. STAGES-1 (prologue) and kb-2+STAGES
+        // (refills), so slab kb has min(STAGES-1 (first) or STAGES-2, rest)
+        // newer copies behind it
+        publish(kb == 0 ? min(STAGES - 1, nkb - 1) : min(STAGES - 2, nkb - kb - 1));
+        Frags f;
+        load_frags(stage_ref(u), f);
+        if (kb >= 1 && kb - 1 + STAGES < nkb) issue_slab(kb - 1 + STAGES, stage_ref((u + STAGES - 1) % STAGES));
+        mfma_phase(f);
       }
     }
   }
@@ -404,14 +391,304 @@ void gemm_kernel(GemmArgs p) {
   }
 }
 
-template <int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool DBUF>
+template <int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 static int launch_gemm(GemmArgs a, hipStream_t s) {
   a.tiles_n = (a.n + BN - 1) / BN;
   a.tiles_m = (a.m + BM - 1) / BM;
   const int64_t grid = a.tiles_m * a.tiles_n;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_kernel<MODE, BM, BN, WAVES_M, WAVES_N, STAGES, DBUF>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((gemm_kernel<MODE, BM, BN, WAVES_M, WAVES_N, STAGES>), dim3((unsigned)grid),
                      dim3(64 * WAVES_M * WAVES_N), 0, s, a);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Warp-specialized 256 x 128 tile: 4 MFMA waves + 4 copy waves.
+//
+// Measured on gfx950: a copy of 1 KB (buffer_load ... lds or a plain vector
+// load) holds its wave for ~70-100 issue cycles, so a wave that both copies
+// and multiplies spends most of a slab issuing copies, and the MFMA pipe
+// idles while the waves of a workgroup copy in lockstep.  The MFMAs of one
+// wave per SIMD, on the other hand, run at the full rate (one 16x16x128 FP8
+// MFMA per 32 cycles) while another wave on the same SIMD copies, loads or
+// reads LDS.  So the roles are split: waves 0-3 (one per SIMD) only read
+// fragments and run MFMAs and the per-slab rescale, each on a 128 x 64 patch
+// (8 x 4 tiles of 16 x 16, accumulators 128 VGPRs); waves 4-7 only copy
+// slabs into a 3-deep LDS ring (each stage its own LDS object, so the
+// compiler sees that a copy never touches the slab being read).
+//
+// Phase kb (one barrier at its start): the MFMA waves multiply slab kb; the
+// copy waves start the copies of slab kb + 2 into the stage slab kb - 1 left
+// (every MFMA wave finished reading it before this barrier), then wait until
+// their copies of slab kb + 1 have landed.  Every wave passes the same
+// number of barriers.
+//
+// Fragment reads: A rows (and B rows in the forward / weight-gradient
+// layouts) are 128-byte LDS rows of 16-byte chunks, chunk c of row r at
+// c ^ ((r >> 1) & 7); the activation-gradient B slab is stored as copied
+// ([k][n]) and gathered with ds_read_b64_tr_b8 as in gemm_kernel.
+// ---------------------------------------------------------------------------
+template <int MODE, int MW>
+__global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
+  // MW MFMA waves: 4 (one per SIMD, 128 x 64 patches) or 8 (two per SIMD,
+  // 64 x 64 patches, so one wave's rescale VALU work runs under the other's
+  // MFMAs; register budget 168 per lane for three waves per SIMD)
+  constexpr int BM = 256, BN = 128;
+  constexpr int WAVES_N = 2;
+  constexpr int WM = MW == 4 ? 128 : 64, WN = 64, TM = WM / 16, TN = 4;
+  static_assert(MODE == kFprop || MODE == kDgrad || MODE == kWgrad, "dense modes only");
+  static_assert(MW == 4 || MW == 8, "MFMA wave count");
+
+  Stage<BM, BN>& st0 = lds_stage<BM, BN, 0>();
+  Stage<BM, BN>& st1 = lds_stage<BM, BN, 1>();
+  Stage<BM, BN>& st2 = lds_stage<BM, BN, 2>();
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
+  const int l16 = lane & 15, g = lane >> 4;
+
+  const int64_t tile = blockIdx.x;
+  const int64_t tn = tile / p.tiles_m, tm = tile - tn * p.tiles_m;
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int64_t M = p.m, N = p.n, K = p.k;
+  const int nkb = (int)(K / BK);
+  const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+  const int64_t rows_b = N - n0 < BN ? N - n0 : BN;
+
+  if (wave >= MW) {
+    // ======================= copy waves ==========================================
+    const int c = wave - MW;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.qa + m0 * K, rows_a * K);
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa + m0 * nkb, rows_a * nkb * 4);
+    __amdgpu_buffer_rsrc_t rb, rsb;
+    if (MODE == kDgrad) {
+      rb = make_rsrc(p.qb + n0, K * N - n0);
+      rsb = make_rsrc(p.sb, (K / 128) * (N / 128) * 4);
+    } else if (MODE == kWgrad) {
+      rb = make_rsrc(p.qb + n0 * K, rows_b * K);
+      rsb = make_rsrc(p.sb + n0 * nkb, rows_b * nkb * 4);
+    } else {
+      rb = make_rsrc(p.qb + n0 * K, rows_b * K);
+      rsb = make_rsrc(p.sb, (N / 128) * nkb * 4);
+    }
+    // A copy j (8 rows of 128 bytes) = 64 lanes x 16 bytes; lane (row r8,
+    // chunk pc) writes LDS chunk pc of row 8j + r8 from global chunk
+    // pc ^ ((row >> 1) & 7).  The swizzle of row 8j + r8 does not depend on
+    // which j (j = c + 4i keeps (8j >> 1) & 7 = 4c & 7), so one lane offset
+    // serves every copy of this wave and the copy index goes into the scalar
+    // offset.
+    const int crow = 8 * c + (lane >> 3);
+    const int cchunk = (lane & 7) ^ ((crow >> 1) & 7);
+    const uint32_t voff_a = (uint32_t)(crow * K + (cchunk << 4));
+    const uint32_t voff_b = MODE == kDgrad ? (uint32_t)(crow * N + (cchunk << 4)) : voff_a;
+    // scale jobs: wave c copies A rows 64c .. 64c+63; waves 0 and 1 also B columns 64c .. 64c+63
+    const uint32_t voff_sa = (uint32_t)((64 * c + lane) * nkb) * 4u;
+    const int scol = 64 * c + lane;
+    uint32_t voff_sb = 0;
+    if (MODE == kWgrad) {
+      voff_sb = (uint32_t)(scol * nkb) * 4u;
+    } else {
+      const int64_t nb = min((n0 + (scol & 127)) / 128, N / 128 - 1);   // clipped past the edge
+      voff_sb = (uint32_t)(MODE == kDgrad ? nb : nb * nkb) * 4u;
+    }
+    const int my_jobs = 8 + 4 + 1 + (c < 2 ? 1 : 0);
+    auto issue = [&](int kb, Stage<BM, BN>& s) {
+      const uint32_t ks = (uint32_t)kb * BK;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)                                   // A copies j = c + 4i
+        dma16(ra, s.a + (c + 4 * i) * 1024, voff_a, ks + (uint32_t)(32 * i) * (uint32_t)K);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {                                 // B copies j = c + 4i
+        if (MODE == kDgrad)
+          dma16(rb, s.b + (c + 4 * i) * 1024, voff_b, (ks + (uint32_t)(32 * i)) * (uint32_t)N);
+        else
+          dma16(rb, s.b + (c + 4 * i) * 1024, voff_b, ks + (uint32_t)(32 * i) * (uint32_t)K);
+      }
+      dma4(rsa, s.sa + 64 * c, voff_sa, (uint32_t)kb * 4u);
+      if (c < 2) {
+        if (MODE == kDgrad)
+          dma4(rsb, s.sb + 64 * c, voff_sb, (uint32_t)kb * (uint32_t)(N / 128) * 4u);
+        else
+          dma4(rsb, s.sb + 64 * c, voff_sb, (uint32_t)kb * 4u);
+      }
+    };
+    auto barrier = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    // prologue: slabs 0 and 1; slab 0 landed before the first barrier
+    issue(0, st0);
+    if (nkb > 1) {
+      issue(1, st1);
+      wait_vmcnt_dyn(my_jobs);
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier();
+    // the MFMA waves pass one barrier per slab (at its start), so the copy
+    // waves pass the prologue barrier plus one per phase except the last
+    auto phase = [&](int kb, Stage<BM, BN>& fill) {
+      if (kb + 2 < nkb) {
+        issue(kb + 2, fill);
+        wait_vmcnt_dyn(my_jobs);                                    // slab kb + 1 landed
+      } else {
+        wait_vmcnt<0>();
+      }
+      if (kb + 1 < nkb) barrier();
+    };
+    for (int kb = 0; kb < nkb; kb += 3) {
+      phase(kb, st2);
+      if (kb + 1 < nkb) phase(kb + 1, st0);
+      if (kb + 2 < nkb) phase(kb + 2, st1);
+    }
+    return;
+  }
+
+  // ========================= MFMA waves ==========================================
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int ra0 = WM * wm + l16, rb0 = WN * wn + l16;
+  const int a_lo = ra0 * BK + (((2 * g) ^ ((ra0 >> 1) & 7)) << 4);
+  const int a_hi = ra0 * BK + (((2 * g + 1) ^ ((ra0 >> 1) & 7)) << 4);
+  const int b_lo = rb0 * BK + (((2 * g) ^ ((rb0 >> 1) & 7)) << 4);
+  const int b_hi = rb0 * BK + (((2 * g + 1) ^ ((rb0 >> 1) & 7)) << 4);
+  auto frag = [&](const uint8_t* base, int lo, int hi, int t) -> v8i {
+    const uint4 x = *reinterpret_cast<const uint4*>(base + lo + t * 16 * BK);
+    const uint4 y = *reinterpret_cast<const uint4*>(base + hi + t * 16 * BK);
+    return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+  };
+  // dgrad: rows of the B slab are k; lane (g, l16) gathers k = 32g .. 32g+31 of
+  // column WN*wn + 16i + l16 with ds_read_b64_tr_b8
+  auto frag_b_tr = [&](const uint8_t* base, int i) -> v8i {
+    const int col16 = (WN * wn + 16 * i) >> 4;
+    const int half = (l16 & 1) << 3;
+    v2i part[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 32 * g + 8 * q + (l16 >> 1);
+      part[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i*)(base + swz(row, col16) + half));
+    }
+    return v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
+  };
+
+  v4f acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  auto slab = [&](const Stage<BM, BN>& s) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    v8i bf[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) bf[i] = MODE == kDgrad ? frag_b_tr(s.b, i) : frag(s.b, b_lo, b_hi, i);
+    v4f wb[TN];
+    float wb0 = 0.f;
+    if (MODE == kWgrad) {
+#pragma unroll
+      for (int i = 0; i < TN; ++i) wb[i] = *reinterpret_cast<const v4f*>(&s.sb[WN * wn + 16 * i + 4 * g]);
+    } else {
+      wb0 = s.sb[WN * wn];                  // one weight block covers the tile's 128 columns
+    }
+    // rescale of tile t runs after the MFMA of tile t + 1 (its result is
+    // ready by then); a scheduling barrier after each pair keeps the
+    // compiler from batching MFMA results, which would cost 4 VGPRs each
+    v4f P_prev = zero;
+    float w_prev = 0.f;
+    auto rescale = [&](int t, const v4f& P, float wa) {
+      const int i = t % TN, j = t / TN;
+      if (MODE == kWgrad) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(wa * wb[i][v], P[v], acc[i][j][v]);
+      } else {
+        const float w = wa * wb0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(w, P[v], acc[i][j][v]);
+      }
+    };
+    v8i a_cur = frag(s.a, a_lo, a_hi, 0);
+    float wa_cur = s.sa[WM * wm + l16];
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      v8i a_nxt = a_cur;
+      float wa_nxt = wa_cur;
+      if (j + 1 < TM) {
+        a_nxt = frag(s.a, a_lo, a_hi, j + 1);
+        wa_nxt = s.sa[WM * wm + 16 * (j + 1) + l16];
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int t = j * TN + i;
+        const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[i], a_cur, zero, 0, 0, 0, 0, 0, 0);
+        if (t > 0) rescale(t - 1, P_prev, w_prev);
+        P_prev = P;
+        w_prev = wa_cur;
+      }
+      // schedule of this 16-row tile: the LDS reads of the next tile first,
+      // then per MFMA tile: the MFMA, then the rescale of the previous tile
+      // (which by then has its result), so the matrix core never waits on VALU
+      __builtin_amdgcn_sched_group_barrier(0x0100, 3, 0);          // DS reads
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);        // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0002, MODE == kWgrad ? 8 : 4, 0);   // the previous tile's rescale
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      a_cur = a_nxt;
+      wa_cur = wa_nxt;
+    }
+    rescale(TM * TN - 1, P_prev, w_prev);
+  };
+  for (int kb = 0; kb < nkb; kb += 3) {
+    slab(st0);
+    if (kb + 1 < nkb) slab(st1);
+    if (kb + 2 < nkb) slab(st2);
+  }
+
+  // ---- epilogue --------------------------------------------------------------
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int64_t row = m0 + WM * wm + 16 * j + l16;
+    if (row >= M) continue;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int64_t col = n0 + WN * wn + 16 * i + 4 * g;
+      if (col >= N) continue;
+      if (MODE == kWgrad) {
+        float* dst = reinterpret_cast<float*>(p.c) + row * p.ldc + col;
+        float4 o = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        if (p.accumulate) {
+          const float4 old = *reinterpret_cast<const float4*>(dst);
+          o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+        }
+        *reinterpret_cast<float4*>(dst) = o;
+      } else {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + row * p.ldc + col;
+        uint2 o;
+        o.x = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+        o.y = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(dst) = o;
+      }
+    }
+  }
+}
+
+#ifndef FP8BS_WS_MFMA_WAVES
+#define FP8BS_WS_MFMA_WAVES 4
+#endif
+template <int MODE>
+static int launch_gemm_ws(GemmArgs a, hipStream_t s) {
+  constexpr int MW = FP8BS_WS_MFMA_WAVES;
+  a.tiles_n = (a.n + 127) / 128;
+  a.tiles_m = (a.m + 255) / 256;
+  const int64_t grid = a.tiles_m * a.tiles_n;
+  if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
+  hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
   return launch_status();
 }
 
@@ -419,21 +696,49 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 
 using namespace fp8bs;
 
+// Kernel choice.  The warp-specialized 256 x 128 kernel (gemm_ws_kernel) is
+// the faster one per CU, but it runs one tile per CU; when a problem has
+// fewer such tiles than three quarters of the CUs, the 128 x 128 kernel (two
+// tiles per CU) keeps more of the chip busy.  FP8BS_GEMM_TILE=128|256 forces
+// a choice (experiments and tests of both paths).
+static int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+static bool use_ws(int64_t m, int64_t n) {
+  static int forced = -1;
+  if (forced < 0) {
+    const char* e = getenv("FP8BS_GEMM_TILE");
+    forced = e ? atoi(e) : 0;
+  }
+  if (forced == 128) return false;
+  if (forced == 256) return true;
+  const int64_t tiles = ((m + 255) / 256) * ((n + 127) / 128);
+  return 4 * tiles >= 3 * cu_count();
+}
+
 // Offsets inside one operand are 32-bit (buffer addressing): a tile's rows of
 // A or B, and the dgrad weight as a whole, must stay below 4 GiB.
 static bool fits_u32(int64_t bytes) { return bytes < 0xFFFFFFFFLL; }
 
 #ifndef FP8BS_TILE_FPROP
-#define FP8BS_TILE_FPROP 128, 128, 2, 2, 2, false
+#define FP8BS_TILE_FPROP 128, 128, 2, 2, 2
 #endif
 #ifndef FP8BS_TILE_DGRAD
-#define FP8BS_TILE_DGRAD 128, 128, 2, 2, 2, false
+#define FP8BS_TILE_DGRAD 128, 128, 2, 2, 2
 #endif
 #ifndef FP8BS_TILE_WGRAD
-#define FP8BS_TILE_WGRAD 128, 128, 2, 2, 2, false
+#define FP8BS_TILE_WGRAD 128, 128, 2, 2, 2
 #endif
 #ifndef FP8BS_TILE_GROUPED
-#define FP8BS_TILE_GROUPED 128, 128, 2, 2, 2, false
+#define FP8BS_TILE_GROUPED 128, 128, 2, 2, 2
 #endif
 
 extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
@@ -447,6 +752,10 @@ extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb,
       ldc % 8)
     return FP8BS_ERR_ALIGN;
   GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, k, nullptr, 0, 0, 0, 0};
+  if (use_ws(m, n)) {
+    if (b_layout == 0) return launch_gemm_ws<kFprop>(a, (hipStream_t)stream);
+    return launch_gemm_ws<kDgrad>(a, (hipStream_t)stream);
+  }
   if (b_layout == 0) return launch_gemm<kFprop, FP8BS_TILE_FPROP>(a, (hipStream_t)stream);
   return launch_gemm<kDgrad, FP8BS_TILE_DGRAD>(a, (hipStream_t)stream);
 }
@@ -477,5 +786,6 @@ extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_
       ldc % 4)
     return FP8BS_ERR_ALIGN;
   GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, t, nullptr, 0, 0, 0, accumulate};
+  if (use_ws(m, n)) return launch_gemm_ws<kWgrad>(a, (hipStream_t)stream);
   return launch_gemm<kWgrad, FP8BS_TILE_WGRAD>(a, (hipStream_t)stream);
 }

@@ -97,6 +97,42 @@ def test_fprop_strided_output_and_determinism(gpu_lib):
 
 # ---------------------------------------------------------------- dgrad -------
 
+def test_large_ragged_shapes_sampled(gpu_lib):
+    """Shapes large enough for the 256 x 128 warp-specialized kernel, with ragged
+    edges: M not a multiple of 256 (forward, dgrad, wgrad) and, for the weight
+    gradient, N not a multiple of 128.  Random codes and scales fed to both
+    sides; the oracle checks sampled rows (including the last ones)."""
+    rng = np.random.default_rng(210)
+    m, n, k = 4096 + 77, 1536 + 128, 1024
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, k // 128)), random_scales(rng, (n // 128, k // 128))
+    rows = _sample_rows(m, 24)
+    got = bf16_values_host(gpu_lib.fp8bs_gemm(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb)))[rows]
+    c64 = gemm_fprop(qa[rows], sa[rows], qb, sb)
+    mag = gemm_fprop(magnitude_codes(qa[rows]), sa[rows], magnitude_codes(qb), sb)
+    assert_gemm_parity(got, c64, mag, label=f"fprop large ragged {m}x{n}x{k}")
+    # dgrad with the [K, N] weight: contraction n, output [m, ko]
+    ko = 2048
+    qw, sw = random_codes(rng, (n, ko)), random_scales(rng, (n // 128, ko // 128))
+    qd, sd = random_codes(rng, (m, n)), random_scales(rng, (m, n // 128))
+    got = bf16_values_host(gpu_lib.fp8bs_gemm(to_dev(qd), to_dev(sd), to_dev(qw), to_dev(sw), b_layout=1))[rows]
+    c64 = gemm_dgrad(qd[rows], sd[rows], qw, sw)
+    mag = gemm_dgrad(magnitude_codes(qd[rows]), sd[rows], magnitude_codes(qw), sw)
+    assert_gemm_parity(got, c64, mag, label=f"dgrad large ragged {m}x{ko}x{n}")
+    # wgrad: C f32 [mw, nw] over t tokens, nw % 128 != 0
+    mw, nw, t = 1536 + 64, 7168 + 36, 1024
+    qa2, qb2 = random_codes(rng, (mw, t)), random_codes(rng, (nw, t))
+    sa2, sb2 = random_scales(rng, (mw, t // 128)), random_scales(rng, (nw, t // 128))
+    out = gpu_lib.fp8bs_gemm_wgrad(to_dev(qa2), to_dev(sa2), to_dev(qb2), to_dev(sb2))
+    torch.cuda.synchronize()
+    wr = _sample_rows(mw, 12)
+    cols = np.unique(np.concatenate([_sample_rows(nw, 64, seed=3), np.arange(nw - 40, nw)]))
+    got = out.cpu().numpy()[np.ix_(wr, cols)].astype(np.float64)
+    c64 = gemm_wgrad(qa2[wr], sa2[wr], qb2[cols], sb2[cols])
+    mag = gemm_wgrad(magnitude_codes(qa2[wr]), sa2[wr], magnitude_codes(qb2[cols]), sb2[cols])
+    assert_gemm_parity(got, c64, mag, out_bf16=False, label=f"wgrad large ragged {mw}x{nw}x{t}")
+
+
 def test_dgrad_random_codes(gpu_lib):
     rng = np.random.default_rng(202)
     for m, k, n in [(3, 128, 128), (130, 256, 384), (256, 384, 256)]:      # contraction k, output n
