@@ -428,16 +428,22 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // c ^ ((r >> 1) & 7); the activation-gradient B slab is stored as copied
 // ([k][n]) and gathered with ds_read_b64_tr_b8 as in gemm_kernel.
 // ---------------------------------------------------------------------------
-template <int MODE, int MW>
+template <int MODE, int MW, int BM>
 __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
-  // MW MFMA waves: 4 (one per SIMD, 128 x 64 patches) or 8 (two per SIMD,
-  // 64 x 64 patches, so one wave's rescale VALU work runs under the other's
-  // MFMAs; register budget 168 per lane for three waves per SIMD)
-  constexpr int BM = 256, BN = 128;
+  // MW MFMA waves: 4 (one per SIMD, (BM/2) x 64 patches) or 8 (two per SIMD,
+  // (BM/4) x 64 patches, so one wave's rescale VALU work runs under the
+  // other's MFMAs; register budget 168 per lane for three waves per SIMD).
+  // BM = 256 or 192 rows: the launcher picks the one that leaves fewer idle
+  // CUs in the last round of tiles.
+  constexpr int BN = 128;
   constexpr int WAVES_N = 2;
-  constexpr int WM = MW == 4 ? 128 : 64, WN = 64, TM = WM / 16, TN = 4;
+  constexpr int WM = BM / (MW / WAVES_N), WN = 64, TM = WM / 16, TN = 4;
+  constexpr int A_CP = BM / 8 / 4;            // A copies (8 rows each) per copy wave
+  constexpr int SA_JOBS = BM / 64;            // 64-row scale copies of A
   static_assert(MODE == kFprop || MODE == kDgrad || MODE == kWgrad, "dense modes only");
   static_assert(MW == 4 || MW == 8, "MFMA wave count");
+  static_assert(BM == 256 || BM == 192, "tile height");
+  static_assert(WM % 16 == 0, "whole MFMA tiles per wave");
 
   Stage<BM, BN>& st0 = lds_stage<BM, BN, 0>();
   Stage<BM, BN>& st1 = lds_stage<BM, BN, 1>();
@@ -482,7 +488,8 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     const int cchunk = (lane & 7) ^ ((crow >> 1) & 7);
     const uint32_t voff_a = (uint32_t)(crow * K + (cchunk << 4));
     const uint32_t voff_b = MODE == kDgrad ? (uint32_t)(crow * N + (cchunk << 4)) : voff_a;
-    // scale jobs: wave c copies A rows 64c .. 64c+63; waves 0 and 1 also B columns 64c .. 64c+63
+    // scale jobs: wave c < SA_JOBS copies A rows 64c .. 64c+63; waves 0 and 1
+    // also B columns 64c .. 64c+63
     const uint32_t voff_sa = (uint32_t)((64 * c + lane) * nkb) * 4u;
     const int scol = 64 * c + lane;
     uint32_t voff_sb = 0;
@@ -492,11 +499,11 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
       const int64_t nb = min((n0 + (scol & 127)) / 128, N / 128 - 1);   // clipped past the edge
       voff_sb = (uint32_t)(MODE == kDgrad ? nb : nb * nkb) * 4u;
     }
-    const int my_jobs = 8 + 4 + 1 + (c < 2 ? 1 : 0);
+    const int my_jobs = A_CP + 4 + (c < SA_JOBS ? 1 : 0) + (c < 2 ? 1 : 0);
     auto issue = [&](int kb, Stage<BM, BN>& s) {
       const uint32_t ks = (uint32_t)kb * BK;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)                                   // A copies j = c + 4i
+      for (int i = 0; i < A_CP; ++i)                                // A copies j = c + 4i
         dma16(ra, s.a + (c + 4 * i) * 1024, voff_a, ks + (uint32_t)(32 * i) * (uint32_t)K);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {                                 // B copies j = c + 4i
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
         else
           dma16(rb, s.b + (c + 4 * i) * 1024, voff_b, ks + (uint32_t)(32 * i) * (uint32_t)K);
       }
-      dma4(rsa, s.sa + 64 * c, voff_sa, (uint32_t)kb * 4u);
+      if (c < SA_JOBS) dma4(rsa, s.sa + 64 * c, voff_sa, (uint32_t)kb * 4u);
       if (c < 2) {
         if (MODE == kDgrad)
           dma4(rsb, s.sb + 64 * c, voff_sb, (uint32_t)kb * (uint32_t)(N / 128) * 4u);
@@ -682,13 +689,21 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
 #define FP8BS_WS_MFMA_WAVES 4
 #endif
 template <int MODE>
-static int launch_gemm_ws(GemmArgs a, hipStream_t s) {
+static int launch_gemm_ws(GemmArgs a, hipStream_t s, int cus) {
   constexpr int MW = FP8BS_WS_MFMA_WAVES;
   a.tiles_n = (a.n + 127) / 128;
-  a.tiles_m = (a.m + 255) / 256;
+  // tile height: rounds of one tile per CU times the tile height, smaller
+  // wins; a 192-row tile does ~10% less per cycle (smaller MFMA patches read
+  // more LDS per MFMA), so its cost is weighted by 11/10
+  const int64_t t256 = ((a.m + 255) / 256) * a.tiles_n, t192 = ((a.m + 191) / 192) * a.tiles_n;
+  const bool tall = ((t256 + cus - 1) / cus) * 256 * 10 <= ((t192 + cus - 1) / cus) * 192 * 11;
+  a.tiles_m = tall ? (a.m + 255) / 256 : (a.m + 191) / 192;
   const int64_t grid = a.tiles_m * a.tiles_n;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
+  if (tall)
+    hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 256>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 192>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
   return launch_status();
 }
 
@@ -753,8 +768,8 @@ extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb,
     return FP8BS_ERR_ALIGN;
   GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, k, nullptr, 0, 0, 0, 0};
   if (use_ws(m, n)) {
-    if (b_layout == 0) return launch_gemm_ws<kFprop>(a, (hipStream_t)stream);
-    return launch_gemm_ws<kDgrad>(a, (hipStream_t)stream);
+    if (b_layout == 0) return launch_gemm_ws<kFprop>(a, (hipStream_t)stream, cu_count());
+    return launch_gemm_ws<kDgrad>(a, (hipStream_t)stream, cu_count());
   }
   if (b_layout == 0) return launch_gemm<kFprop, FP8BS_TILE_FPROP>(a, (hipStream_t)stream);
   return launch_gemm<kDgrad, FP8BS_TILE_DGRAD>(a, (hipStream_t)stream);
@@ -786,6 +801,6 @@ extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_
       ldc % 4)
     return FP8BS_ERR_ALIGN;
   GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, t, nullptr, 0, 0, 0, accumulate};
-  if (use_ws(m, n)) return launch_gemm_ws<kWgrad>(a, (hipStream_t)stream);
+  if (use_ws(m, n)) return launch_gemm_ws<kWgrad>(a, (hipStream_t)stream, cu_count());
   return launch_gemm<kWgrad, FP8BS_TILE_WGRAD>(a, (hipStream_t)stream);
 }
