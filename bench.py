@@ -431,9 +431,14 @@ def main():
     gemm_flops = sum(c.flops for c in calls)
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
 
-    # per-kernel durations (second timed region, same stream discipline)
-    for c, ms in zip(calls, time_kernels(calls, state, rotate, args.kernel_reps)):
-        c.times_ms.append(ms)
+    # per-kernel durations (second timed region, same stream discipline);
+    # --kernel-reps 0 skips it (profiler runs), leaving the step average per call
+    if args.kernel_reps > 0:
+        for c, ms in zip(calls, time_kernels(calls, state, rotate, args.kernel_reps)):
+            c.times_ms.append(ms)
+    else:
+        for c in calls:
+            c.times_ms.append(ms_per_step / len(calls))
     kernel_sum_us = sum(c.times_ms[0] for c in calls) * 1e3
 
     kernels = {}
