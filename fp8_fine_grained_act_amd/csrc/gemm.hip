@@ -61,7 +61,35 @@ struct GemmArgs {
   int64_t num_experts;
   int64_t tiles_m, tiles_n;
   int accumulate;
+  int64_t group_m;  // band height in m-tiles of the XCD-aware order; 0 = plain order
 };
+
+// Workgroups are dealt to the chip's 8 XCDs round-robin by workgroup id, and
+// each XCD has its own L2.  With group_m > 0 the id is first remapped so that
+// every XCD owns one contiguous range of logical tiles; logical tiles then
+// walk down M inside bands of group_m m-tiles, so one XCD's range covers a
+// compact block of about group_m tile rows by range/group_m tile columns,
+// and the A rows and B columns its L2 must hold stay few.  With group_m = 0
+// consecutive workgroups walk down M inside one N column.
+constexpr int kXcds = 8;
+__device__ inline void tile_coords(const GemmArgs& p, int64_t b, int64_t& tm, int64_t& tn) {
+  if (p.group_m <= 0) {
+    tn = b / p.tiles_m;
+    tm = b - tn * p.tiles_m;
+    return;
+  }
+  const int64_t tiles = p.tiles_m * p.tiles_n;
+  const int64_t per = (tiles + kXcds - 1) / kXcds;   // XCDs own ranges of per or per - 1 tiles
+  const int64_t full = tiles - kXcds * (per - 1);    // how many own per (1..8)
+  const int64_t x = b % kXcds, j = b / kXcds;
+  const int64_t l = x < full ? x * per + j : full * per + (x - full) * (per - 1) + j;
+  const int64_t band_tiles = p.group_m * p.tiles_n;
+  const int64_t band = l / band_tiles, r = l - band * band_tiles;
+  const int64_t first = band * p.group_m;
+  const int64_t rows = p.tiles_m - first < p.group_m ? p.tiles_m - first : p.group_m;
+  tn = r / rows;
+  tm = first + (r - tn * rows);
+}
 
 constexpr int BK = 128;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access, gfx9 family
@@ -157,10 +185,8 @@ void gemm_kernel(GemmArgs p) {
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int l16 = lane & 15, g = lane >> 4;
 
-  // tile order: consecutive workgroups walk down M inside one N column, so a
-  // column of B stays hot in L2 while the A rows stream past
-  const int64_t tile = blockIdx.x;
-  const int64_t tn = tile / p.tiles_m, tm = tile - tn * p.tiles_m;
+  int64_t tm, tn;
+  tile_coords(p, blockIdx.x, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t M = p.m, N = p.n, K = p.k;
   const int nkb = (int)(K / BK);
@@ -391,10 +417,62 @@ void gemm_kernel(GemmArgs p) {
   }
 }
 
+// Band height of the XCD-aware tile order (tile_coords).  Each XCD fetches
+// the A tile rows and B tile columns its range of tiles touches; this picks
+// the height (1..32 m-tiles) that minimises their sum, BM and BN bytes per
+// k-byte of a tile row and column, counted exactly per range.  Problems whose
+// output outweighs twice their operands keep the plain order: there the
+// banded order leaves the XCDs writing narrow column windows a fixed stride
+// apart, which measured up to 2x slower on a 4096 x 32768 x 512 forward GEMM
+// (the order changes nothing else for them).
+// FP8BS_GEMM_GROUP_M=<h> forces a height, and -1 the plain order.
+static int64_t range_cost(int64_t tiles_m, int64_t tiles_n, int64_t bm, int64_t bn, int64_t gm) {
+  const int64_t tiles = tiles_m * tiles_n;
+  const int64_t per = (tiles + kXcds - 1) / kXcds, full = tiles - kXcds * (per - 1);
+  const int64_t band_tiles = gm * tiles_n;
+  int64_t cost = 0, l = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    int64_t l0 = l;
+    const int64_t l1 = l + (x < full ? per : per - 1);
+    l = l1;
+    while (l0 < l1) {                       // pieces of the range, one per band
+      const int64_t band = l0 / band_tiles, first = band * gm;
+      const int64_t rows = tiles_m - first < gm ? tiles_m - first : gm;
+      const int64_t a = l0 - band * band_tiles;
+      const int64_t b = l1 - band * band_tiles < rows * tiles_n ? l1 - band * band_tiles : rows * tiles_n;
+      const int64_t cols = (b - 1) / rows - a / rows + 1;
+      const int64_t rws = rows < b - a ? rows : b - a;
+      cost += rws * bm + cols * bn;
+      l0 = band * band_tiles + b;
+    }
+  }
+  return cost;
+}
+static int64_t choose_group_m(const GemmArgs& a, int64_t bm, int64_t bn, int64_t out_bytes) {
+  static int forced = -2;
+  if (forced == -2) {
+    const char* e = getenv("FP8BS_GEMM_GROUP_M");
+    forced = e ? atoi(e) : 0;
+  }
+  const int64_t tiles_m = a.tiles_m, tiles_n = a.tiles_n;
+  if (forced < 0) return 0;
+  if (forced > 0) return forced < tiles_m ? forced : tiles_m;
+  if ((double)a.m * (double)a.n * (double)out_bytes > 2.0 * (double)(a.m + a.n) * (double)a.k) return 0;
+  int64_t best = 1, best_cost = -1;
+  const int64_t hi = tiles_m < 32 ? tiles_m : 32;
+  for (int64_t gm = 1; gm <= hi; ++gm) {
+    const int64_t c = range_cost(tiles_m, tiles_n, bm, bn, gm);
+    if (best_cost < 0 || c < best_cost) best = gm, best_cost = c;
+  }
+  return best;
+}
+
 template <int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 static int launch_gemm(GemmArgs a, hipStream_t s) {
   a.tiles_n = (a.n + BN - 1) / BN;
   a.tiles_m = (a.m + BM - 1) / BM;
+  // the grouped GEMM keeps the plain order: its B depends on the row segment
+  a.group_m = MODE == kGrouped ? 0 : choose_group_m(a, BM, BN, MODE == kWgrad ? 4 : 2);
   const int64_t grid = a.tiles_m * a.tiles_n;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
   hipLaunchKernelGGL((gemm_kernel<MODE, BM, BN, WAVES_M, WAVES_N, STAGES>), dim3((unsigned)grid),
@@ -454,8 +532,8 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
   const int l16 = lane & 15, g = lane >> 4;
 
-  const int64_t tile = blockIdx.x;
-  const int64_t tn = tile / p.tiles_m, tm = tile - tn * p.tiles_m;
+  int64_t tm, tn;
+  tile_coords(p, blockIdx.x, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t M = p.m, N = p.n, K = p.k;
   const int nkb = (int)(K / BK);
@@ -698,6 +776,7 @@ static int launch_gemm_ws(GemmArgs a, hipStream_t s, int cus) {
   const int64_t t256 = ((a.m + 255) / 256) * a.tiles_n, t192 = ((a.m + 191) / 192) * a.tiles_n;
   const bool tall = ((t256 + cus - 1) / cus) * 256 * 10 <= ((t192 + cus - 1) / cus) * 192 * 11;
   a.tiles_m = tall ? (a.m + 255) / 256 : (a.m + 191) / 192;
+  a.group_m = choose_group_m(a, tall ? 256 : 192, 128, MODE == kWgrad ? 4 : 2);
   const int64_t grid = a.tiles_m * a.tiles_n;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
   if (tall)
@@ -766,7 +845,7 @@ extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb,
   if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
       ldc % 8)
     return FP8BS_ERR_ALIGN;
-  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, k, nullptr, 0, 0, 0, 0};
+  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, k, nullptr, 0, 0, 0, 0, 0};
   if (use_ws(m, n)) {
     if (b_layout == 0) return launch_gemm_ws<kFprop>(a, (hipStream_t)stream, cu_count());
     return launch_gemm_ws<kDgrad>(a, (hipStream_t)stream, cu_count());
@@ -786,7 +865,7 @@ extern "C" int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int3
   if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
       !aligned(seg_offsets, 4))
     return FP8BS_ERR_ALIGN;
-  GemmArgs a{qa, sa, qb, sb, c, n, total_rows, n, k, seg_offsets, num_experts, 0, 0, 0};
+  GemmArgs a{qa, sa, qb, sb, c, n, total_rows, n, k, seg_offsets, num_experts, 0, 0, 0, 0};
   return launch_gemm<kGrouped, FP8BS_TILE_GROUPED>(a, (hipStream_t)stream);
 }
 
@@ -800,7 +879,7 @@ extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_
   if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
       ldc % 4)
     return FP8BS_ERR_ALIGN;
-  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, t, nullptr, 0, 0, 0, accumulate};
+  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, t, nullptr, 0, 0, 0, accumulate, 0};
   if (use_ws(m, n)) return launch_gemm_ws<kWgrad>(a, (hipStream_t)stream, cu_count());
   return launch_gemm<kWgrad, FP8BS_TILE_WGRAD>(a, (hipStream_t)stream);
 }

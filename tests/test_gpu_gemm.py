@@ -133,6 +133,47 @@ def test_large_ragged_shapes_sampled(gpu_lib):
     assert_gemm_parity(got, c64, mag, out_bf16=False, label=f"wgrad large ragged {mw}x{nw}x{t}")
 
 
+def test_xcd_banded_tile_order_full_outputs(gpu_lib):
+    """Shapes whose operands outweigh half their output, so the launch walks the
+    tiles in the XCD-aware banded order: tile counts that do not split evenly
+    over 8 XCDs (221, 399) and bands whose last one is shorter (17 m-tiles in
+    bands of 5), on both GEMM kernels.  The output is filled with NaN first and
+    every element is compared with the oracle, so a tile mapped twice or never
+    fails."""
+    rng = np.random.default_rng(211)
+
+    def nan_bf16(m, n):
+        return torch.full((m, n), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+    for m, n, k in [(4173, 1664, 1280), (1000, 640, 2048)]:
+        qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+        sa, sb = random_scales(rng, (m, k // 128)), random_scales(rng, (n // 128, k // 128))
+        c = nan_bf16(m, n)
+        gpu_lib.fp8bs_gemm(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), c=c)
+        got = bf16_values_host(c)
+        c64 = gemm_fprop(qa, sa, qb, sb)
+        mag = gemm_fprop(magnitude_codes(qa), sa, magnitude_codes(qb), sb)
+        assert_gemm_parity(got, c64, mag, label=f"fprop banded order {m}x{n}x{k}")
+    m, kc, ko = 1000, 1536, 768           # dgrad: contraction kc, output [m, ko]
+    qd, sd = random_codes(rng, (m, kc)), random_scales(rng, (m, kc // 128))
+    qw, sw = random_codes(rng, (kc, ko)), random_scales(rng, (kc // 128, ko // 128))
+    c = nan_bf16(m, ko)
+    gpu_lib.fp8bs_gemm(to_dev(qd), to_dev(sd), to_dev(qw), to_dev(sw), b_layout=1, c=c)
+    got = bf16_values_host(c)
+    c64 = gemm_dgrad(qd, sd, qw, sw)
+    mag = gemm_dgrad(magnitude_codes(qd), sd, magnitude_codes(qw), sw)
+    assert_gemm_parity(got, c64, mag, label=f"dgrad banded order {m}x{ko}x{kc}")
+    mw, nw, t = 1600, 7204, 4096
+    qa2, qb2 = random_codes(rng, (mw, t)), random_codes(rng, (nw, t))
+    sa2, sb2 = random_scales(rng, (mw, t // 128)), random_scales(rng, (nw, t // 128))
+    out = torch.full((mw, nw), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_lib.fp8bs_gemm_wgrad(to_dev(qa2), to_dev(sa2), to_dev(qb2), to_dev(sb2), c=out)
+    got = out.cpu().numpy().astype(np.float64)
+    c64 = gemm_wgrad(qa2, sa2, qb2, sb2)
+    mag = gemm_wgrad(magnitude_codes(qa2), sa2, magnitude_codes(qb2), sb2)
+    assert_gemm_parity(got, c64, mag, out_bf16=False, label=f"wgrad banded order {mw}x{nw}x{t}")
+
+
 def test_dgrad_random_codes(gpu_lib):
     rng = np.random.default_rng(202)
     for m, k, n in [(3, 128, 128), (130, 256, 384), (256, 384, 256)]:      # contraction k, output n
