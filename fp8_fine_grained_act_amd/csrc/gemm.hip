@@ -495,11 +495,15 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // slabs into a 3-deep LDS ring (each stage its own LDS object, so the
 // compiler sees that a copy never touches the slab being read).
 //
-// Phase kb (one barrier at its start): the MFMA waves multiply slab kb; the
-// copy waves start the copies of slab kb + 2 into the stage slab kb - 1 left
-// (every MFMA wave finished reading it before this barrier), then wait until
-// their copies of slab kb + 1 have landed.  Every wave passes the same
-// number of barriers.
+// Barriers (forward, weight gradient): the MFMA waves multiply slab kb and,
+// in its last 16-row group, once every LDS read of slab kb has returned, pass
+// barrier kb + 1 and read the head of slab kb + 1 (its B fragments, first A
+// fragment and scales) between that group's MFMAs, so no slab starts with an
+// LDS round trip.  Between barriers kb and kb + 1 the copy waves start the
+// copies of slab kb + 2 into the stage slab kb - 1 left (fully read before
+// barrier kb), then wait until their copies of slab kb + 1 have landed.
+// Every wave passes nkb + 1 barriers.  dgrad passes barrier kb at the start
+// of slab kb instead (nkb barriers), see kEarly.
 //
 // Fragment reads: A rows (and B rows in the forward / weight-gradient
 // layouts) are 128-byte LDS rows of 16-byte chunks, chunk c of row r at
@@ -612,8 +616,11 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
       wait_vmcnt<0>();
     }
     barrier();
-    // the MFMA waves pass one barrier per slab (at its start), so the copy
-    // waves pass the prologue barrier plus one per phase except the last
+    // with the early head the MFMA waves pass the prologue barrier plus one
+    // per slab (in its last group), else one per slab (at its start); the
+    // copy waves pass the prologue barrier plus one per phase, except the
+    // last phase in the second case
+    constexpr bool kEarly = MODE != kDgrad;
     auto phase = [&](int kb, Stage<BM, BN>& fill) {
       if (kb + 2 < nkb) {
         issue(kb + 2, fill);
@@ -621,7 +628,7 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
       } else {
         wait_vmcnt<0>();
       }
-      if (kb + 1 < nkb) barrier();
+      if (kEarly || kb + 1 < nkb) barrier();
     };
     for (int kb = 0; kb < nkb; kb += 3) {
       phase(kb, st2);
@@ -664,40 +671,91 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  auto slab = [&](const Stage<BM, BN>& s) {
+  // The head of a slab: what its first 16-row group needs (all B fragments,
+  // the first A fragment, the first row scale, the column scales).  It is read
+  // right after the barrier that publishes the slab, while the MFMAs of the
+  // previous slab's last group still run.
+  struct Head {
+    v8i bf[TN];
+    v8i a0;
+    float wa0;
+    float wb0;      // forward / dgrad: one weight block covers the 128 columns
+    v4f wb[TN];     // weight gradient: a scale per column
+  };
+  // reads in the order of first use: B fragment 0 and A fragment 0 (the
+  // first MFMA), the scales (its fold), then the other B fragments
+  auto read_head = [&](const Stage<BM, BN>& s) {
+    Head h;
+    h.bf[0] = MODE == kDgrad ? frag_b_tr(s.b, 0) : frag(s.b, b_lo, b_hi, 0);
+    h.a0 = frag(s.a, a_lo, a_hi, 0);
+    h.wa0 = s.sa[WM * wm + l16];
+    if (MODE == kWgrad) {
+#pragma unroll
+      for (int i = 0; i < TN; ++i) h.wb[i] = *reinterpret_cast<const v4f*>(&s.sb[WN * wn + 16 * i + 4 * g]);
+      h.wb0 = 0.f;
+    } else {
+      h.wb0 = s.sb[WN * wn];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) h.wb[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 1; i < TN; ++i) h.bf[i] = MODE == kDgrad ? frag_b_tr(s.b, i) : frag(s.b, b_lo, b_hi, i);
+    return h;
+  };
+  // LDS instructions of one head, spread over the MFMAs of the group that
+  // reads it (issued all at once they queue behind each other and hold up
+  // that group's MFMAs)
+  constexpr int kHeadReads = (MODE == kDgrad ? 4 * TN : 2 * TN) + 2 + 1 + (MODE == kWgrad ? TN : 1);
+  constexpr int kHeadPerMfma = (kHeadReads + TN - 1) / TN;
+  auto barrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    v8i bf[TN];
-#pragma unroll
-    for (int i = 0; i < TN; ++i) bf[i] = MODE == kDgrad ? frag_b_tr(s.b, i) : frag(s.b, b_lo, b_hi, i);
-    v4f wb[TN];
-    float wb0 = 0.f;
+  };
+
+  // Rescale lag: the partial of each MFMA tile is folded into its accumulator
+  // after the next MFMA has been issued (its result is ready by then); the
+  // lag runs across slabs, so a slab's first MFMA also has independent VALU
+  // work beside it.  pw (times pwb per column for the weight gradient) is the
+  // pending partial's weight, (pi, pj) its tile.
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  v4f P_prev = zero;
+  float pw = 0.f;
+  v4f pwb = zero;
+  auto fold = [&](int i, int j) {
     if (MODE == kWgrad) {
 #pragma unroll
-      for (int i = 0; i < TN; ++i) wb[i] = *reinterpret_cast<const v4f*>(&s.sb[WN * wn + 16 * i + 4 * g]);
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(pw * pwb[v], P_prev[v], acc[i][j][v]);
     } else {
-      wb0 = s.sb[WN * wn];                  // one weight block covers the tile's 128 columns
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(pw, P_prev[v], acc[i][j][v]);
     }
-    // rescale of tile t runs after the MFMA of tile t + 1 (its result is
-    // ready by then); a scheduling barrier after each pair keeps the
-    // compiler from batching MFMA results, which would cost 4 VGPRs each
-    v4f P_prev = zero;
-    float w_prev = 0.f;
-    auto rescale = [&](int t, const v4f& P, float wa) {
-      const int i = t % TN, j = t / TN;
-      if (MODE == kWgrad) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(wa * wb[i][v], P[v], acc[i][j][v]);
-      } else {
-        const float w = wa * wb0;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(w, P[v], acc[i][j][v]);
-      }
-    };
-    v8i a_cur = frag(s.a, a_lo, a_hi, 0);
-    float wa_cur = s.sa[WM * wm + l16];
+  };
+
+  // Early head (forward, weight gradient): barrier kb + 1 sits in the last
+  // group of slab kb and the head of slab kb + 1 is read under that group's
+  // MFMAs.  dgrad keeps the barrier at the start of each slab: its head is
+  // 16 transposing LDS reads, more than one group's MFMAs hide, and it
+  // measured 7% slower with the early head.
+  constexpr bool kEarly = MODE != kDgrad;
+  Head hd;
+  if (kEarly) {
+    barrier();                                 // slab 0 landed
+    hd = read_head(st0);
+  }
+
+  // Slab kb from stage s; the last group passes barrier kb + 1 (every LDS read
+  // of slab kb has returned by then, so the copy waves may refill its stage)
+  // and reads the head of slab kb + 1 from stage sn.  After the final slab
+  // that head is never used.
+  auto slab = [&](const Stage<BM, BN>& s, const Stage<BM, BN>& sn) {
+    if (!kEarly) {
+      barrier();
+      hd = read_head(s);
+    }
+    v8i a_cur = hd.a0;
+    float wa_cur = hd.wa0;
+    Head nx;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       v8i a_nxt = a_cur;
@@ -705,35 +763,54 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
       if (j + 1 < TM) {
         a_nxt = frag(s.a, a_lo, a_hi, j + 1);
         wa_nxt = s.sa[WM * wm + 16 * (j + 1) + l16];
+      } else if (kEarly) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0): slab kb fully read
+        barrier();
+        nx = read_head(sn);
       }
+      const float wj = MODE == kWgrad ? wa_cur : wa_cur * hd.wb0;
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
         const int t = j * TN + i;
-        const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[i], a_cur, zero, 0, 0, 0, 0, 0, 0);
-        if (t > 0) rescale(t - 1, P_prev, w_prev);
+        const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hd.bf[i], a_cur, zero, 0, 0, 0, 0, 0, 0);
+        // t = 0 folds the previous slab's last tile (before slab 0: a zero
+        // partial of weight 0 into a zero accumulator, which changes nothing)
+        if (t > 0) fold((t - 1) % TN, (t - 1) / TN);
+        else fold(TN - 1, TM - 1);
         P_prev = P;
-        w_prev = wa_cur;
+        pw = wj;
+        if (MODE == kWgrad) pwb = hd.wb[i];
       }
-      // schedule of this 16-row tile: the LDS reads of the next tile first,
-      // then per MFMA tile: the MFMA, then the rescale of the previous tile
-      // (which by then has its result), so the matrix core never waits on VALU
-      __builtin_amdgcn_sched_group_barrier(0x0100, 3, 0);          // DS reads
+      // per 16-row group: the LDS reads of the next group first, then per
+      // MFMA tile the MFMA and the fold of the previous tile; in the last
+      // group the head reads of the next slab go between the MFMAs
+      if (j + 1 < TM || !kEarly) {
+        if (j + 1 < TM) __builtin_amdgcn_sched_group_barrier(0x0100, 3, 0); // DS reads
 #pragma unroll
-      for (int i = 0; i < TN; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);        // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x0002, MODE == kWgrad ? 8 : 4, 0);   // the previous tile's rescale
+        for (int i = 0; i < TN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);               // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x0002, MODE == kWgrad ? 8 : 4, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x0100, kHeadPerMfma, 0);
+          __builtin_amdgcn_sched_group_barrier(0x0002, MODE == kWgrad ? 8 : 4, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       a_cur = a_nxt;
       wa_cur = wa_nxt;
     }
-    rescale(TM * TN - 1, P_prev, w_prev);
+    if (kEarly) hd = nx;
   };
   for (int kb = 0; kb < nkb; kb += 3) {
-    slab(st0);
-    if (kb + 1 < nkb) slab(st1);
-    if (kb + 2 < nkb) slab(st2);
+    slab(st0, st1);
+    if (kb + 1 < nkb) slab(st1, st2);
+    if (kb + 2 < nkb) slab(st2, st0);
   }
+  fold(TN - 1, TM - 1);
 
   // ---- epilogue --------------------------------------------------------------
 #pragma unroll
