@@ -25,9 +25,9 @@
 //     flight; no VGPRs hold staged data, and rows past the matrix edge read as
 //     zero (buffer range check).  Each stage is its own LDS object, so the
 //     compiler can tell a slab being filled from the slab being read.
-//   * LDS rows are 128 bytes of 16-byte chunks; chunk c of row r is stored at
-//     chunk c ^ ((r >> 1) & 7).  A 16-lane pass of ds_read_b128 then reads 16
-//     distinct 16-byte bank groups (two rows fill the 64 banks).
+//   * LDS rows are 128 bytes of 16-byte chunks, stored with a per-row XOR
+//     swizzle of the chunk index (swz, swz_t below) that keeps every LDS pass
+//     of the fragment reads on 64 distinct banks.
 //   * MFMA src0 carries B rows (output columns n), src1 carries A rows (output
 //     rows m): each lane ends with one output row and four consecutive output
 //     columns -- one 8-byte (bf16) or 16-byte (f32) store.
@@ -108,10 +108,29 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)lds, 4, (int)voff, (int)soff, 0, 0);
 }
 
-// byte offset of 16-byte chunk `chunk` of LDS row `row` (rows of 128 bytes)
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4);
-}
+// LDS bank layout, measured on gfx950 (bank-conflict counter, one lane pair
+// at a time): 64 banks of 4 bytes; ds_read_b128 serves 16 lanes per pass,
+// lanes 0-3, 12-15, 20-23 and 24-27 forming one pass (within each half
+// wave, the 4-lane groups whose index has even bit parity form one pass and
+// the others the second); ds_read_b64 and ds_read_b64_tr_b8 serve 32
+// consecutive lanes per pass.  A pass is conflict-free when its lanes cover
+// 64 distinct banks.
+//
+// Operand rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r is
+// stored at chunk c ^ h(r).  MFMA fragments read with ds_read_b128 (lane
+// group g takes chunks 2g, 2g + 1 of rows l16 = 0..15) are conflict-free with
+// h(r) = (r >> 1) & 5: in every pass the even rows, and the odd rows, land on
+// 8 distinct chunks.  The dgrad weight slab (rows = k, read with
+// ds_read_b64_tr_b8 at rows 32g + 8q + (l16 >> 1)) needs rows r and r + 32
+// apart as well: h_t(r) = ((r >> 1) & 3) | ((r >> 3) & 4).  Measured on the
+// read patterns alone: 202 B/clk/CU for the fragment reads (113 with the
+// earlier (r >> 1) & 7), 147 for the transposing reads (112).
+__device__ __forceinline__ int swz_h(int row) { return (row >> 1) & 5; }
+__device__ __forceinline__ int swz_ht(int row) { return ((row >> 1) & 3) | ((row >> 3) & 4); }
+// byte offset of 16-byte chunk `chunk` of LDS row `row`, fragment layout
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_h(row)) << 4); }
+// the same in the dgrad weight layout
+__device__ __forceinline__ int swz_t(int row, int chunk) { return row * BK + ((chunk ^ swz_ht(row)) << 4); }
 
 // s_waitcnt with only a vmcnt limit (expcnt, lgkmcnt left unconstrained)
 template <int N>
@@ -230,12 +249,12 @@ void gemm_kernel(GemmArgs p) {
     if (q < C::A_CP) {
       const int j = q * NW + wave;
       const int c = j * 64 + lane, row = c >> 3, pc = c & 7;
-      const int lc = pc ^ ((row >> 1) & 7);
+      const int lc = pc ^ swz_h(row);
       dma16(ra, s.a + j * 1024, (uint32_t)(row * K + (lc << 4)), ks);
     } else if (q < C::A_CP + C::B_CP) {
       const int j = (q - C::A_CP) * NW + wave;
       const int c = j * 64 + lane, row = c >> 3, pc = c & 7;
-      const int lc = pc ^ ((row >> 1) & 7);
+      const int lc = pc ^ (MODE == kDgrad ? swz_ht(row) : swz_h(row));
       if (MODE == kDgrad)
         dma16(rb, s.b + j * 1024, (uint32_t)(row * N + (lc << 4)), ks * (uint32_t)N);
       else
@@ -293,7 +312,7 @@ void gemm_kernel(GemmArgs p) {
         for (int q = 0; q < 4; ++q) {
           const int row = 32 * g + 8 * q + (l16 >> 1);
           part[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) v2i*)(&s.b[swz(row, col16) + half]));
+              (__attribute__((address_space(3))) v2i*)(&s.b[swz_t(row, col16) + half]));
         }
         f.bf[i] = v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
       } else {
@@ -506,9 +525,9 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // of slab kb instead (nkb barriers), see kEarly.
 //
 // Fragment reads: A rows (and B rows in the forward / weight-gradient
-// layouts) are 128-byte LDS rows of 16-byte chunks, chunk c of row r at
-// c ^ ((r >> 1) & 7); the activation-gradient B slab is stored as copied
-// ([k][n]) and gathered with ds_read_b64_tr_b8 as in gemm_kernel.
+// layouts) are 128-byte LDS rows of 16-byte chunks in the swz layout; the
+// activation-gradient B slab is stored as copied ([k][n], swz_t layout) and
+// gathered with ds_read_b64_tr_b8 as in gemm_kernel.
 // ---------------------------------------------------------------------------
 template <int MODE, int MW, int BM>
 __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
@@ -562,14 +581,17 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     }
     // A copy j (8 rows of 128 bytes) = 64 lanes x 16 bytes; lane (row r8,
     // chunk pc) writes LDS chunk pc of row 8j + r8 from global chunk
-    // pc ^ ((row >> 1) & 7).  The swizzle of row 8j + r8 does not depend on
-    // which j (j = c + 4i keeps (8j >> 1) & 7 = 4c & 7), so one lane offset
-    // serves every copy of this wave and the copy index goes into the scalar
-    // offset.
+    // pc ^ swz_h(row).  This wave copies j = c + 4i, rows 8c + 32i + r8,
+    // whose swizzle does not depend on i, so one lane offset serves every
+    // copy and the copy index goes into the scalar offset.  The dgrad weight
+    // slab is copied in blocks instead (rows 32c + 8i + r8), for which
+    // swz_ht does not depend on i.
     const int crow = 8 * c + (lane >> 3);
-    const int cchunk = (lane & 7) ^ ((crow >> 1) & 7);
+    const int cchunk = (lane & 7) ^ swz_h(crow);
     const uint32_t voff_a = (uint32_t)(crow * K + (cchunk << 4));
-    const uint32_t voff_b = MODE == kDgrad ? (uint32_t)(crow * N + (cchunk << 4)) : voff_a;
+    const int crow_t = 32 * c + (lane >> 3);
+    const int cchunk_t = (lane & 7) ^ swz_ht(crow_t);
+    const uint32_t voff_b = MODE == kDgrad ? (uint32_t)(crow_t * N + (cchunk_t << 4)) : voff_a;
     // scale jobs: wave c < SA_JOBS copies A rows 64c .. 64c+63; waves 0 and 1
     // also B columns 64c .. 64c+63
     const uint32_t voff_sa = (uint32_t)((64 * c + lane) * nkb) * 4u;
@@ -588,9 +610,9 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
       for (int i = 0; i < A_CP; ++i)                                // A copies j = c + 4i
         dma16(ra, s.a + (c + 4 * i) * 1024, voff_a, ks + (uint32_t)(32 * i) * (uint32_t)K);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {                                 // B copies j = c + 4i
+      for (int i = 0; i < 4; ++i) {                                 // B copies j = c + 4i (dgrad: 4c + i)
         if (MODE == kDgrad)
-          dma16(rb, s.b + (c + 4 * i) * 1024, voff_b, (ks + (uint32_t)(32 * i)) * (uint32_t)N);
+          dma16(rb, s.b + (4 * c + i) * 1024, voff_b, (ks + (uint32_t)(8 * i)) * (uint32_t)N);
         else
           dma16(rb, s.b + (c + 4 * i) * 1024, voff_b, ks + (uint32_t)(32 * i) * (uint32_t)K);
       }
@@ -641,10 +663,9 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   // ========================= MFMA waves ==========================================
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int ra0 = WM * wm + l16, rb0 = WN * wn + l16;
-  const int a_lo = ra0 * BK + (((2 * g) ^ ((ra0 >> 1) & 7)) << 4);
-  const int a_hi = ra0 * BK + (((2 * g + 1) ^ ((ra0 >> 1) & 7)) << 4);
-  const int b_lo = rb0 * BK + (((2 * g) ^ ((rb0 >> 1) & 7)) << 4);
-  const int b_hi = rb0 * BK + (((2 * g + 1) ^ ((rb0 >> 1) & 7)) << 4);
+  // rows ra0 + 16t share ra0's swizzle, so tile t adds 16t rows
+  const int a_lo = swz(ra0, 2 * g), a_hi = swz(ra0, 2 * g + 1);
+  const int b_lo = swz(rb0, 2 * g), b_hi = swz(rb0, 2 * g + 1);
   auto frag = [&](const uint8_t* base, int lo, int hi, int t) -> v8i {
     const uint4 x = *reinterpret_cast<const uint4*>(base + lo + t * 16 * BK);
     const uint4 y = *reinterpret_cast<const uint4*>(base + hi + t * 16 * BK);
@@ -660,7 +681,7 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     for (int q = 0; q < 4; ++q) {
       const int row = 32 * g + 8 * q + (l16 >> 1);
       part[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (__attribute__((address_space(3))) v2i*)(base + swz(row, col16) + half));
+          (__attribute__((address_space(3))) v2i*)(base + swz_t(row, col16) + half));
     }
     return v8i{part[0].x, part[0].y, part[1].x, part[1].y, part[2].x, part[2].y, part[3].x, part[3].y};
   };
@@ -840,12 +861,13 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   }
 }
 
-#ifndef FP8BS_WS_MFMA_WAVES
-#define FP8BS_WS_MFMA_WAVES 4
-#endif
+// MFMA waves per workgroup: two per SIMD for the forward and dgrad GEMMs
+// (one wave's fold and LDS reads issue under the other's MFMAs: forward
+// 4096x1536x7168 61.5 -> 56.7 us); one per SIMD for the weight gradient,
+// whose 8-instruction fold per MFMA does not fit 168 VGPRs without spills.
 template <int MODE>
 static int launch_gemm_ws(GemmArgs a, hipStream_t s, int cus) {
-  constexpr int MW = FP8BS_WS_MFMA_WAVES;
+  constexpr int MW = MODE == kWgrad ? 4 : 8;
   a.tiles_n = (a.n + 127) / 128;
   // tile height: rounds of one tile per CU times the tile height, smaller
   // wins; a 192-row tile does ~10% less per cycle (smaller MFMA patches read
