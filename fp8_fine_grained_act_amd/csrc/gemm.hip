@@ -61,7 +61,7 @@ struct GemmArgs {
   int64_t num_experts;
   int64_t tiles_m, tiles_n;
   int accumulate;
-  int64_t group_m;  // band height in m-tiles of the XCD-aware order; 0 = plain order
+  int64_t group_m;  // band height in m-tiles of the XCD-aware order; 0 = column-major, -1 = row-major
 };
 
 // Workgroups are dealt to the chip's 8 XCDs round-robin by workgroup id, and
@@ -70,12 +70,18 @@ struct GemmArgs {
 // walk down M inside bands of group_m m-tiles, so one XCD's range covers a
 // compact block of about group_m tile rows by range/group_m tile columns,
 // and the A rows and B columns its L2 must hold stay few.  With group_m = 0
-// consecutive workgroups walk down M inside one N column.
+// consecutive workgroups walk down M inside one N column, with -1 along N
+// inside one M row.
 constexpr int kXcds = 8;
 __device__ inline void tile_coords(const GemmArgs& p, int64_t b, int64_t& tm, int64_t& tn) {
-  if (p.group_m <= 0) {
+  if (p.group_m == 0) {
     tn = b / p.tiles_m;
     tm = b - tn * p.tiles_m;
+    return;
+  }
+  if (p.group_m == -1) {            // row-major: all N tiles of one M tile in a row
+    tm = b / p.tiles_n;
+    tn = b - tm * p.tiles_n;
     return;
   }
   const int64_t tiles = p.tiles_m * p.tiles_n;
@@ -490,8 +496,12 @@ template <int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 static int launch_gemm(GemmArgs a, hipStream_t s) {
   a.tiles_n = (a.n + BN - 1) / BN;
   a.tiles_m = (a.m + BM - 1) / BM;
-  // the grouped GEMM keeps the plain order: its B depends on the row segment
-  a.group_m = MODE == kGrouped ? 0 : choose_group_m(a, BM, BN, MODE == kWgrad ? 4 : 2);
+  // grouped GEMM: row-major, so an M tile's rows (one expert's tokens) stay
+  // in L2 across its N tiles and the expert's next M tile follows one row of
+  // tiles later, while that expert's weight columns are still cached
+  // (measured on 256 experts of 4096x7168: 4.09 -> 2.55 ms against the
+  // column-major order, which re-reads every expert's rows once per N tile)
+  a.group_m = MODE == kGrouped ? -1 : choose_group_m(a, BM, BN, MODE == kWgrad ? 4 : 2);
   const int64_t grid = a.tiles_m * a.tiles_n;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
   hipLaunchKernelGGL((gemm_kernel<MODE, BM, BN, WAVES_M, WAVES_N, STAGES>), dim3((unsigned)grid),
