@@ -539,22 +539,26 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // activation-gradient B slab is stored as copied ([k][n], swz_t layout) and
 // gathered with ds_read_b64_tr_b8 as in gemm_kernel.
 // ---------------------------------------------------------------------------
-template <int MODE, int MW, int BM>
+template <int MODE, int MW, int BM, int BN>
 __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
-  // MW MFMA waves: 4 (one per SIMD, (BM/2) x 64 patches) or 8 (two per SIMD,
-  // (BM/4) x 64 patches, so one wave's rescale VALU work runs under the
-  // other's MFMAs; register budget 168 per lane for three waves per SIMD).
-  // BM = 256 or 192 rows: the launcher picks the one that leaves fewer idle
-  // CUs in the last round of tiles.
-  constexpr int BN = 128;
-  constexpr int WAVES_N = 2;
-  constexpr int WM = BM / (MW / WAVES_N), WN = 64, TM = WM / 16, TN = 4;
+  // MW MFMA waves: 4 (one per SIMD) or 8 (two per SIMD, so one wave's
+  // rescale VALU work runs under the other's MFMAs; register budget 168 per
+  // lane for three waves per SIMD), BN / 64 of them across N, each a WM x 64
+  // patch.  Tiles: 256 x 128 or 192 x 128 (the launcher picks the height
+  // that leaves fewer idle CUs in the last round of tiles), and 128 x 256 for
+  // the grouped GEMM, whose expert segments come in 128-row steps.
+  constexpr int WAVES_N = BN / 64;
+  constexpr int WAVES_M = MW / WAVES_N;
+  constexpr int WM = BM / WAVES_M, WN = 64, TM = WM / 16, TN = 4;
   constexpr int A_CP = BM / 8 / 4;            // A copies (8 rows each) per copy wave
+  constexpr int B_CP = BN / 8 / 4;            // B copies per copy wave
   constexpr int SA_JOBS = BM / 64;            // 64-row scale copies of A
-  static_assert(MODE == kFprop || MODE == kDgrad || MODE == kWgrad, "dense modes only");
+  constexpr int SB_JOBS = BN / 64;            // 64-column scale copies of B
+  static_assert(MODE == kFprop || MODE == kDgrad || MODE == kWgrad || MODE == kGrouped, "mode");
   static_assert(MW == 4 || MW == 8, "MFMA wave count");
-  static_assert(BM == 256 || BM == 192, "tile height");
-  static_assert(WM % 16 == 0, "whole MFMA tiles per wave");
+  static_assert((BN == 128 && (BM == 256 || BM == 192)) || (BN == 256 && BM == 128 && MODE != kDgrad),
+                "tile shape");
+  static_assert(WAVES_M * WAVES_N == MW && WM % 16 == 0, "whole MFMA tiles per wave");
 
   Stage<BM, BN>& st0 = lds_stage<BM, BN, 0>();
   Stage<BM, BN>& st1 = lds_stage<BM, BN, 1>();
@@ -576,18 +580,31 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   if (wave >= MW) {
     // ======================= copy waves ==========================================
     const int c = wave - MW;
+    const uint8_t* qb = p.qb;
+    const float* sb = p.sb;
+    if (MODE == kGrouped) {
+      // expert whose segment holds row m0: the largest e with seg[e] <= m0
+      int lo = 0, hi = (int)p.num_experts;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)p.seg[mid] <= m0) lo = mid; else hi = mid - 1;
+      }
+      lo = min(lo, (int)p.num_experts - 1);
+      qb += (int64_t)lo * N * K;
+      sb += (int64_t)lo * (N / 128) * nkb;
+    }
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.qa + m0 * K, rows_a * K);
     const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa + m0 * nkb, rows_a * nkb * 4);
     __amdgpu_buffer_rsrc_t rb, rsb;
     if (MODE == kDgrad) {
-      rb = make_rsrc(p.qb + n0, K * N - n0);
-      rsb = make_rsrc(p.sb, (K / 128) * (N / 128) * 4);
+      rb = make_rsrc(qb + n0, K * N - n0);
+      rsb = make_rsrc(sb, (K / 128) * (N / 128) * 4);
     } else if (MODE == kWgrad) {
-      rb = make_rsrc(p.qb + n0 * K, rows_b * K);
-      rsb = make_rsrc(p.sb + n0 * nkb, rows_b * nkb * 4);
+      rb = make_rsrc(qb + n0 * K, rows_b * K);
+      rsb = make_rsrc(sb + n0 * nkb, rows_b * nkb * 4);
     } else {
-      rb = make_rsrc(p.qb + n0 * K, rows_b * K);
-      rsb = make_rsrc(p.sb, (N / 128) * nkb * 4);
+      rb = make_rsrc(qb + n0 * K, rows_b * K);
+      rsb = make_rsrc(sb, (N / 128) * nkb * 4);
     }
     // A copy j (8 rows of 128 bytes) = 64 lanes x 16 bytes; lane (row r8,
     // chunk pc) writes LDS chunk pc of row 8j + r8 from global chunk
@@ -602,32 +619,32 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     const int crow_t = 32 * c + (lane >> 3);
     const int cchunk_t = (lane & 7) ^ swz_ht(crow_t);
     const uint32_t voff_b = MODE == kDgrad ? (uint32_t)(crow_t * N + (cchunk_t << 4)) : voff_a;
-    // scale jobs: wave c < SA_JOBS copies A rows 64c .. 64c+63; waves 0 and 1
-    // also B columns 64c .. 64c+63
+    // scale jobs: wave c < SA_JOBS copies A rows 64c .. 64c+63, wave
+    // c < SB_JOBS also B columns 64c .. 64c+63
     const uint32_t voff_sa = (uint32_t)((64 * c + lane) * nkb) * 4u;
     const int scol = 64 * c + lane;
     uint32_t voff_sb = 0;
     if (MODE == kWgrad) {
       voff_sb = (uint32_t)(scol * nkb) * 4u;
     } else {
-      const int64_t nb = min((n0 + (scol & 127)) / 128, N / 128 - 1);   // clipped past the edge
+      const int64_t nb = min((n0 + scol) / 128, N / 128 - 1);   // clipped past the edge
       voff_sb = (uint32_t)(MODE == kDgrad ? nb : nb * nkb) * 4u;
     }
-    const int my_jobs = A_CP + 4 + (c < SA_JOBS ? 1 : 0) + (c < 2 ? 1 : 0);
+    const int my_jobs = A_CP + B_CP + (c < SA_JOBS ? 1 : 0) + (c < SB_JOBS ? 1 : 0);
     auto issue = [&](int kb, Stage<BM, BN>& s) {
       const uint32_t ks = (uint32_t)kb * BK;
 #pragma unroll
       for (int i = 0; i < A_CP; ++i)                                // A copies j = c + 4i
         dma16(ra, s.a + (c + 4 * i) * 1024, voff_a, ks + (uint32_t)(32 * i) * (uint32_t)K);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {                                 // B copies j = c + 4i (dgrad: 4c + i)
+      for (int i = 0; i < B_CP; ++i) {                              // B copies j = c + 4i (dgrad: 4c + i)
         if (MODE == kDgrad)
           dma16(rb, s.b + (4 * c + i) * 1024, voff_b, (ks + (uint32_t)(8 * i)) * (uint32_t)N);
         else
           dma16(rb, s.b + (c + 4 * i) * 1024, voff_b, ks + (uint32_t)(32 * i) * (uint32_t)K);
       }
       if (c < SA_JOBS) dma4(rsa, s.sa + 64 * c, voff_sa, (uint32_t)kb * 4u);
-      if (c < 2) {
+      if (c < SB_JOBS) {
         if (MODE == kDgrad)
           dma4(rsb, s.sb + 64 * c, voff_sb, (uint32_t)kb * (uint32_t)(N / 128) * 4u);
         else
@@ -889,9 +906,21 @@ static int launch_gemm_ws(GemmArgs a, hipStream_t s, int cus) {
   const int64_t grid = a.tiles_m * a.tiles_n;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
   if (tall)
-    hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 256>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
+    hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 256, 128>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 192>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
+    hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 192, 128>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
+  return launch_status();
+}
+
+// Grouped GEMM on 128 x 256 tiles (n % 256 == 0), 8 MFMA waves, row-major
+// tile order (see launch_gemm).
+static int launch_grouped_ws(GemmArgs a, hipStream_t s) {
+  a.tiles_n = a.n / 256;
+  a.tiles_m = a.m / 128;
+  a.group_m = -1;
+  const int64_t grid = a.tiles_m * a.tiles_n;
+  if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
+  hipLaunchKernelGGL((gemm_ws_kernel<kGrouped, 8, 128, 256>), dim3((unsigned)grid), dim3(64 * 12), 0, s, a);
   return launch_status();
 }
 
@@ -975,6 +1004,7 @@ extern "C" int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int3
       !aligned(seg_offsets, 4))
     return FP8BS_ERR_ALIGN;
   GemmArgs a{qa, sa, qb, sb, c, n, total_rows, n, k, seg_offsets, num_experts, 0, 0, 0, 0};
+  if (n % 256 == 0) return launch_grouped_ws(a, (hipStream_t)stream);
   return launch_gemm<kGrouped, FP8BS_TILE_GROUPED>(a, (hipStream_t)stream);
 }
 

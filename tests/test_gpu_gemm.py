@@ -278,17 +278,20 @@ def test_grouped_small_end_to_end(gpu_lib):
 
 
 def test_grouped_empty_and_single_expert(gpu_lib):
+    """Empty segments, one expert owning every row; n = 128 runs the 128 x 128
+    kernel, n = 512 the 128 x 256 warp-specialized one."""
     rng = np.random.default_rng(205)
-    n, k = 128, 256
+    k = 256
     qa, sa = random_codes(rng, (384, k)), random_scales(rng, (384, k // 128))
-    qb, sb = random_codes(rng, (4, n, k)), random_scales(rng, (4, n // 128, k // 128))
-    for off in ([0, 0, 384, 384, 384], [0, 128, 128, 256, 384], [0, 384, 384, 384, 384]):
-        off = np.array(off)
-        c = gpu_lib.fp8bs_grouped_gemm(to_dev(qa), to_dev(sa), to_dev(off.astype(np.int32)), to_dev(qb),
-                                       to_dev(sb))
-        c64 = grouped_gemm(qa, sa, off, qb, sb)
-        mag = grouped_gemm(magnitude_codes(qa), sa, off, magnitude_codes(qb), sb)
-        assert_gemm_parity(bf16_values_host(c), c64, mag, label=f"grouped offsets {off.tolist()}")
+    for n in (128, 512):
+        qb, sb = random_codes(rng, (4, n, k)), random_scales(rng, (4, n // 128, k // 128))
+        for off in ([0, 0, 384, 384, 384], [0, 128, 128, 256, 384], [0, 384, 384, 384, 384]):
+            off = np.array(off)
+            c = gpu_lib.fp8bs_grouped_gemm(to_dev(qa), to_dev(sa), to_dev(off.astype(np.int32)), to_dev(qb),
+                                           to_dev(sb))
+            c64 = grouped_gemm(qa, sa, off, qb, sb)
+            mag = grouped_gemm(magnitude_codes(qa), sa, off, magnitude_codes(qb), sb)
+            assert_gemm_parity(bf16_values_host(c), c64, mag, label=f"grouped n={n} offsets {off.tolist()}")
 
 
 def test_grouped_c4_full_launch_sampled_experts(gpu_lib):
