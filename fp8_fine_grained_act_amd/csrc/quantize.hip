@@ -71,9 +71,8 @@ __global__ __launch_bounds__(256) void quant_act_rows_kernel(
 // writes its 32 codes as two 16-byte stores.  Each 16-lane group codes two
 // column quads.
 //
-// Row tiles (ROWS) read whole rows with ds_read_b128: a group of 16 lanes is
-// 16 consecutive rows (distinct f(R), no conflict), each lane half a row;
-// the other half sits 16 lanes away.
+// Row tiles (ROWS) read half rows with ds_read_b128, mapped onto the read's
+// lane passes so that no pass reads a chunk position twice (see below).
 // ---------------------------------------------------------------------------
 constexpr int kQB = 128;                   // rows and columns per square
 
@@ -101,7 +100,8 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
   const int64_t rblk = kQOrder ? blockIdx.x : blockIdx.y;
   const int64_t c0 = (int64_t)(kQOrder ? blockIdx.y : blockIdx.x) * kQB;
   const int64_t first = rblk * kQGroups * kQB;                 // rows % 128 == 0: squares are full
-  const int nsq = (int)min<int64_t>(kQGroups, (rows - first) / kQB);
+  // squares of this block (at least one: rows % 128 == 0 and the grid is exact)
+  const int nsq = kQGroups == 1 ? 1 : (int)min<int64_t>(kQGroups, (rows - first) / kQB);
 
   // staging lanes: thread (chunk, rr) covers rows rr, rr+16, ... at 16-byte chunk `chunk`.
   // A chunk past the last column (cols % 8 == 0, so chunks are whole) loads a valid
@@ -165,10 +165,15 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
       }
     }
 
-    // ---- row tiles (fused mode, cols % 128 == 0): 16 consecutive rows per group, half a row per lane
+    // ---- row tiles (fused mode, cols % 128 == 0): half a row per lane.  A
+    // ds_read_b128 pass serves the 4-lane groups of one index parity within
+    // a half wave (measured: lanes 0-3, 12-15, 20-23, 24-27 share a pass), so
+    // the half hh is that parity: each pass reads one half of 16 distinct
+    // rows, 16 distinct chunks.  The other half of a row is 4 lanes away.
     if (ROWS) {
-      const int hh = (tid >> 4) & 1;
-      const int r = lane + 16 * (tid >> 5);
+      const int quad = (tid >> 2) & 7;
+      const int hh = (quad ^ (quad >> 1) ^ (quad >> 2)) & 1;
+      const int r = 16 * (tid >> 5) + 4 * ((tid >> 3) & 3) + (tid & 3);
       uint4 w[8];
       uint32_t m2 = 0;
 #pragma unroll
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
                                      max_u16x2(w[j].z & 0x7FFF7FFFu, w[j].w & 0x7FFF7FFFu)));
       }
       uint32_t m = max(m2 & 0xFFFFu, m2 >> 16);
-      m = max(m, (uint32_t)__shfl_xor((int)m, 16));            // the other half of the row
+      m = max(m, (uint32_t)__shfl_xor((int)m, 4));             // the other half of the row
       const GroupScale gs = group_scale(m);
       uint8_t* dst = q + (r0 + r) * ldq + c0 + 64 * hh;
       uint4 o[4];
