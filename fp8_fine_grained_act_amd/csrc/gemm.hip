@@ -73,28 +73,34 @@ struct GemmArgs {
 // consecutive workgroups walk down M inside one N column, with -1 along N
 // inside one M row.
 constexpr int kXcds = 8;
-__device__ inline void tile_coords(const GemmArgs& p, int64_t b, int64_t& tm, int64_t& tn) {
+// Tile counts stay below 2^31 (checked at launch), so the index arithmetic
+// is 32-bit.  Returned by value: through references from several branches
+// the compiler placed (m, n) in scratch memory.
+struct TileMN {
+  uint32_t m, n;
+};
+__device__ inline TileMN tile_coords(const GemmArgs& p, uint32_t b) {
+  const uint32_t tiles_m = (uint32_t)p.tiles_m, tiles_n = (uint32_t)p.tiles_n;
   if (p.group_m == 0) {
-    tn = b / p.tiles_m;
-    tm = b - tn * p.tiles_m;
-    return;
+    const uint32_t n = b / tiles_m;
+    return TileMN{b - n * tiles_m, n};
   }
   if (p.group_m == -1) {            // row-major: all N tiles of one M tile in a row
-    tm = b / p.tiles_n;
-    tn = b - tm * p.tiles_n;
-    return;
+    const uint32_t m = b / tiles_n;
+    return TileMN{m, b - m * tiles_n};
   }
-  const int64_t tiles = p.tiles_m * p.tiles_n;
-  const int64_t per = (tiles + kXcds - 1) / kXcds;   // XCDs own ranges of per or per - 1 tiles
-  const int64_t full = tiles - kXcds * (per - 1);    // how many own per (1..8)
-  const int64_t x = b % kXcds, j = b / kXcds;
-  const int64_t l = x < full ? x * per + j : full * per + (x - full) * (per - 1) + j;
-  const int64_t band_tiles = p.group_m * p.tiles_n;
-  const int64_t band = l / band_tiles, r = l - band * band_tiles;
-  const int64_t first = band * p.group_m;
-  const int64_t rows = p.tiles_m - first < p.group_m ? p.tiles_m - first : p.group_m;
-  tn = r / rows;
-  tm = first + (r - tn * rows);
+  const uint32_t gm = (uint32_t)p.group_m;
+  const uint32_t tiles = tiles_m * tiles_n;
+  const uint32_t per = (tiles + kXcds - 1) / kXcds;   // XCDs own ranges of per or per - 1 tiles
+  const uint32_t full = tiles - kXcds * (per - 1);    // how many own per (1..8)
+  const uint32_t x = b % kXcds, j = b / kXcds;
+  const uint32_t l = x < full ? x * per + j : full * per + (x - full) * (per - 1) + j;
+  const uint32_t band_tiles = gm * tiles_n;
+  const uint32_t band = l / band_tiles, r = l - band * band_tiles;
+  const uint32_t first = band * gm;
+  const uint32_t rows = tiles_m - first < gm ? tiles_m - first : gm;
+  const uint32_t n = r / rows;
+  return TileMN{first + (r - n * rows), n};
 }
 
 constexpr int BK = 128;
@@ -210,9 +216,8 @@ void gemm_kernel(GemmArgs p) {
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int l16 = lane & 15, g = lane >> 4;
 
-  int64_t tm, tn;
-  tile_coords(p, blockIdx.x, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const TileMN tc = tile_coords(p, blockIdx.x);
+  const int64_t m0 = (int64_t)tc.m * BM, n0 = (int64_t)tc.n * BN;
   const int64_t M = p.m, N = p.n, K = p.k;
   const int nkb = (int)(K / BK);
 
@@ -539,7 +544,7 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // activation-gradient B slab is stored as copied ([k][n], swz_t layout) and
 // gathered with ds_read_b64_tr_b8 as in gemm_kernel.
 // ---------------------------------------------------------------------------
-template <int MODE, int MW, int BM, int BN>
+template <int MODE, int MW, int BM, int BN, bool PERSIST>
 __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   // MW MFMA waves: 4 (one per SIMD) or 8 (two per SIMD, so one wave's
   // rescale VALU work runs under the other's MFMAs; register budget 168 per
@@ -569,43 +574,74 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
   const int l16 = lane & 15, g = lane >> 4;
 
-  int64_t tm, tn;
-  tile_coords(p, blockIdx.x, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
+  // Persistent: workgroup w takes tiles w, w + G, w + 2G, ... (G = gridDim.x,
+  // a multiple of 8 whenever a workgroup gets more than one tile, so all its
+  // tiles stay on its own XCD and tile_coords' XCD-aware order holds) and
+  // walks them as one sequence of slab units: unit u is slab u % nkb of its
+  // (u / nkb)-th tile.  The LDS ring and the barriers run across tile
+  // boundaries, so the next tile's first slabs are copied while the MFMA
+  // waves store the previous tile.
   const int64_t M = p.m, N = p.n, K = p.k;
   const int nkb = (int)(K / BK);
-  const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
-  const int64_t rows_b = N - n0 < BN ? N - n0 : BN;
+  // PERSIST = false: one tile per workgroup (grid = tiles), with the tile
+  // bookkeeping and the store outside the slab loop, which keeps the MFMA
+  // waves' registers as in a plain kernel.
+  const int64_t G = gridDim.x;
+  const int my_tiles = PERSIST ? (int)((p.tiles_m * p.tiles_n - 1 - (int64_t)blockIdx.x) / G + 1) : 1;
+  const int units = my_tiles * nkb;
+  struct Origin {
+    int64_t m0, n0;
+  };
+  auto tile_origin = [&](int i) {
+    const TileMN t = tile_coords(p, (uint32_t)((int64_t)blockIdx.x + (int64_t)i * G));
+    return Origin{(int64_t)t.m * BM, (int64_t)t.n * BN};
+  };
 
   if (wave >= MW) {
     // ======================= copy waves ==========================================
     const int c = wave - MW;
-    const uint8_t* qb = p.qb;
-    const float* sb = p.sb;
-    if (MODE == kGrouped) {
-      // expert whose segment holds row m0: the largest e with seg[e] <= m0
-      int lo = 0, hi = (int)p.num_experts;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)p.seg[mid] <= m0) lo = mid; else hi = mid - 1;
+    // per-tile copy state: buffer resources (ranges clip ragged edges to zeros)
+    // and the weight-scale offset of this wave's columns
+    __amdgpu_buffer_rsrc_t ra, rsa, rb, rsb;
+    uint32_t voff_sb = 0;
+    const int scol = 64 * c + lane;
+    auto set_tile = [&](int i) {
+      const Origin o = tile_origin(i);
+      const int64_t m0 = o.m0, n0 = o.n0;
+      const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+      const int64_t rows_b = N - n0 < BN ? N - n0 : BN;
+      const uint8_t* qb = p.qb;
+      const float* sb = p.sb;
+      if (MODE == kGrouped) {
+        // expert whose segment holds row m0: the largest e with seg[e] <= m0
+        int lo = 0, hi = (int)p.num_experts;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if ((int64_t)p.seg[mid] <= m0) lo = mid; else hi = mid - 1;
+        }
+        lo = min(lo, (int)p.num_experts - 1);
+        qb += (int64_t)lo * N * K;
+        sb += (int64_t)lo * (N / 128) * nkb;
       }
-      lo = min(lo, (int)p.num_experts - 1);
-      qb += (int64_t)lo * N * K;
-      sb += (int64_t)lo * (N / 128) * nkb;
-    }
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.qa + m0 * K, rows_a * K);
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa + m0 * nkb, rows_a * nkb * 4);
-    __amdgpu_buffer_rsrc_t rb, rsb;
-    if (MODE == kDgrad) {
-      rb = make_rsrc(qb + n0, K * N - n0);
-      rsb = make_rsrc(sb, (K / 128) * (N / 128) * 4);
-    } else if (MODE == kWgrad) {
-      rb = make_rsrc(qb + n0 * K, rows_b * K);
-      rsb = make_rsrc(sb + n0 * nkb, rows_b * nkb * 4);
-    } else {
-      rb = make_rsrc(qb + n0 * K, rows_b * K);
-      rsb = make_rsrc(sb, (N / 128) * nkb * 4);
-    }
+      ra = make_rsrc(p.qa + m0 * K, rows_a * K);
+      rsa = make_rsrc(p.sa + m0 * nkb, rows_a * nkb * 4);
+      if (MODE == kDgrad) {
+        rb = make_rsrc(qb + n0, K * N - n0);
+        rsb = make_rsrc(sb, (K / 128) * (N / 128) * 4);
+      } else if (MODE == kWgrad) {
+        rb = make_rsrc(qb + n0 * K, rows_b * K);
+        rsb = make_rsrc(sb + n0 * nkb, rows_b * nkb * 4);
+      } else {
+        rb = make_rsrc(qb + n0 * K, rows_b * K);
+        rsb = make_rsrc(sb, (N / 128) * nkb * 4);
+      }
+      if (MODE == kWgrad) {
+        voff_sb = (uint32_t)(scol * nkb) * 4u;
+      } else {
+        const int64_t nb = min((n0 + scol) / 128, N / 128 - 1);   // clipped past the edge
+        voff_sb = (uint32_t)(MODE == kDgrad ? nb : nb * nkb) * 4u;
+      }
+    };
     // A copy j (8 rows of 128 bytes) = 64 lanes x 16 bytes; lane (row r8,
     // chunk pc) writes LDS chunk pc of row 8j + r8 from global chunk
     // pc ^ swz_h(row).  This wave copies j = c + 4i, rows 8c + 32i + r8,
@@ -620,16 +656,8 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     const int cchunk_t = (lane & 7) ^ swz_ht(crow_t);
     const uint32_t voff_b = MODE == kDgrad ? (uint32_t)(crow_t * N + (cchunk_t << 4)) : voff_a;
     // scale jobs: wave c < SA_JOBS copies A rows 64c .. 64c+63, wave
-    // c < SB_JOBS also B columns 64c .. 64c+63
+    // c < SB_JOBS also B columns 64c .. 64c+63 (voff_sb, set per tile)
     const uint32_t voff_sa = (uint32_t)((64 * c + lane) * nkb) * 4u;
-    const int scol = 64 * c + lane;
-    uint32_t voff_sb = 0;
-    if (MODE == kWgrad) {
-      voff_sb = (uint32_t)(scol * nkb) * 4u;
-    } else {
-      const int64_t nb = min((n0 + scol) / 128, N / 128 - 1);   // clipped past the edge
-      voff_sb = (uint32_t)(MODE == kDgrad ? nb : nb * nkb) * 4u;
-    }
     const int my_jobs = A_CP + B_CP + (c < SA_JOBS ? 1 : 0) + (c < SB_JOBS ? 1 : 0);
     auto issue = [&](int kb, Stage<BM, BN>& s) {
       const uint32_t ks = (uint32_t)kb * BK;
@@ -656,33 +684,43 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
-    // prologue: slabs 0 and 1; slab 0 landed before the first barrier
-    issue(0, st0);
-    if (nkb > 1) {
-      issue(1, st1);
+    // units are issued in order: tile `it`, slab `ikb` next
+    int it = 0, ikb = 0;
+    set_tile(0);
+    auto issue_next = [&](Stage<BM, BN>& s) {
+      if (PERSIST && ikb == nkb) {
+        ikb = 0;
+        set_tile(++it);
+      }
+      issue(ikb++, s);
+    };
+    // prologue: units 0 and 1; unit 0 landed before the first barrier
+    issue_next(st0);
+    if (units > 1) {
+      issue_next(st1);
       wait_vmcnt_dyn(my_jobs);
     } else {
       wait_vmcnt<0>();
     }
     barrier();
     // with the early head the MFMA waves pass the prologue barrier plus one
-    // per slab (in its last group), else one per slab (at its start); the
+    // per unit (in its last group), else one per unit (at its start); the
     // copy waves pass the prologue barrier plus one per phase, except the
     // last phase in the second case
     constexpr bool kEarly = MODE != kDgrad;
-    auto phase = [&](int kb, Stage<BM, BN>& fill) {
-      if (kb + 2 < nkb) {
-        issue(kb + 2, fill);
-        wait_vmcnt_dyn(my_jobs);                                    // slab kb + 1 landed
+    auto phase = [&](int u, Stage<BM, BN>& fill) {
+      if (u + 2 < units) {
+        issue_next(fill);
+        wait_vmcnt_dyn(my_jobs);                                    // unit u + 1 landed
       } else {
         wait_vmcnt<0>();
       }
-      if (kEarly || kb + 1 < nkb) barrier();
+      if (kEarly || u + 1 < units) barrier();
     };
-    for (int kb = 0; kb < nkb; kb += 3) {
-      phase(kb, st2);
-      if (kb + 1 < nkb) phase(kb + 1, st0);
-      if (kb + 2 < nkb) phase(kb + 2, st1);
+    for (int u = 0; u < units; u += 3) {
+      phase(u, st2);
+      if (u + 1 < units) phase(u + 1, st0);
+      if (u + 2 < units) phase(u + 2, st1);
     }
     return;
   }
@@ -853,39 +891,80 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     }
     if (kEarly) hd = nx;
   };
-  for (int kb = 0; kb < nkb; kb += 3) {
-    slab(st0, st1);
-    if (kb + 1 < nkb) slab(st1, st2);
-    if (kb + 2 < nkb) slab(st2, st0);
-  }
-  fold(TN - 1, TM - 1);
-
-  // ---- epilogue --------------------------------------------------------------
+  // ---- tile end: fold the pending partial, store, start the next tile ------
+  Origin org = tile_origin(0);
+  auto store_tile = [&]() {
+    const int64_t m0 = org.m0, n0 = org.n0;
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int64_t row = m0 + WM * wm + 16 * j + l16;
-    if (row >= M) continue;
+    for (int j = 0; j < TM; ++j) {
+      const int64_t row = m0 + WM * wm + 16 * j + l16;
+      if (row >= M) continue;
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const int64_t col = n0 + WN * wn + 16 * i + 4 * g;
-      if (col >= N) continue;
-      if (MODE == kWgrad) {
-        float* dst = reinterpret_cast<float*>(p.c) + row * p.ldc + col;
-        float4 o = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        if (p.accumulate) {
-          const float4 old = *reinterpret_cast<const float4*>(dst);
-          o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+      for (int i = 0; i < TN; ++i) {
+        const int64_t col = n0 + WN * wn + 16 * i + 4 * g;
+        if (col >= N) continue;
+        if (MODE == kWgrad) {
+          float* dst = reinterpret_cast<float*>(p.c) + row * p.ldc + col;
+          float4 o = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+          if (p.accumulate) {
+            const float4 old = *reinterpret_cast<const float4*>(dst);
+            o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+          }
+          *reinterpret_cast<float4*>(dst) = o;
+        } else {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + row * p.ldc + col;
+          uint2 o;
+          o.x = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+          o.y = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2*>(dst) = o;
         }
-        *reinterpret_cast<float4*>(dst) = o;
-      } else {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + row * p.ldc + col;
-        uint2 o;
-        o.x = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
-        o.y = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(dst) = o;
       }
+      __builtin_amdgcn_sched_barrier(0);     // one row of stores at a time: few live temporaries
+    }
+  };
+  int ti = 0, tkb = 0;
+  auto after_slab = [&]() {
+    if (!PERSIST || ++tkb < nkb) return;
+    fold(TN - 1, TM - 1);
+    store_tile();
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] = zero;
+    P_prev = zero;                             // the next slab's first fold adds nothing
+    pw = 0.f;
+    pwb = zero;
+    tkb = 0;
+    if (++ti < my_tiles) org = tile_origin(ti);
+  };
+  for (int u = 0; u < units; u += 3) {
+    slab(st0, st1);
+    after_slab();
+    if (u + 1 < units) {
+      slab(st1, st2);
+      after_slab();
+    }
+    if (u + 2 < units) {
+      slab(st2, st0);
+      after_slab();
     }
   }
+  if (!PERSIST) {
+    fold(TN - 1, TM - 1);
+    store_tile();
+  }
+}
+
+// Workgroups of the persistent kernel: one per CU (the LDS ring allows no
+// more), a multiple of 8 so every tile of a workgroup stays on its XCD; 0
+// when a workgroup's unit count (tiles x K slabs) would not fit an int.
+static int64_t persistent_grid(const GemmArgs& a, int cus) {
+  const int64_t tiles = a.tiles_m * a.tiles_n;
+  int64_t g = cus - cus % kXcds;
+  if (g < kXcds) g = kXcds;
+  if (tiles < g) g = tiles;
+  if (tiles > kMaxGrid || ((tiles + g - 1) / g) * (a.k / BK) >= (int64_t)1 << 31) return 0;
+  return g;
 }
 
 // MFMA waves per workgroup: two per SIMD for the forward and dgrad GEMMs
@@ -903,12 +982,27 @@ static int launch_gemm_ws(GemmArgs a, hipStream_t s, int cus) {
   const bool tall = ((t256 + cus - 1) / cus) * 256 * 10 <= ((t192 + cus - 1) / cus) * 192 * 11;
   a.tiles_m = tall ? (a.m + 255) / 256 : (a.m + 191) / 192;
   a.group_m = choose_group_m(a, tall ? 256 : 192, 128, MODE == kWgrad ? 4 : 2);
-  const int64_t grid = a.tiles_m * a.tiles_n;
-  if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
-  if (tall)
-    hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 256, 128>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 192, 128>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
+  const int64_t tiles = a.tiles_m * a.tiles_n;
+  int64_t grid = persistent_grid(a, cus);
+  if (grid <= 0) return FP8BS_ERR_SHAPE;
+  if (MODE == kWgrad && tall) grid = tiles;
+  const dim3 block(64 * (MW + 4));
+  // the persistent form only where a workgroup gets more than one tile
+  // (its in-loop store costs registers: forward 4096x1536x7168, one tile
+  // per workgroup, measured 20% slower with it), and not for the weight
+  // gradient's 256-row tiles, whose persistent form spills (32768x512 over
+  // 4096 tokens: 101 -> 121 us)
+  if (grid < tiles) {
+    if (tall)
+      hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 256, 128, true>), dim3((unsigned)grid), block, 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 192, 128, true>), dim3((unsigned)grid), block, 0, s, a);
+  } else {
+    if (tall)
+      hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 256, 128, false>), dim3((unsigned)grid), block, 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 192, 128, false>), dim3((unsigned)grid), block, 0, s, a);
+  }
   return launch_status();
 }
 
@@ -920,7 +1014,9 @@ static int launch_grouped_ws(GemmArgs a, hipStream_t s) {
   a.group_m = -1;
   const int64_t grid = a.tiles_m * a.tiles_n;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_ws_kernel<kGrouped, 8, 128, 256>), dim3((unsigned)grid), dim3(64 * 12), 0, s, a);
+  // one tile per workgroup: the persistent form measured 9% slower here
+  // (256 experts of 4096x7168), its in-loop store spilling registers
+  hipLaunchKernelGGL((gemm_ws_kernel<kGrouped, 8, 128, 256, false>), dim3((unsigned)grid), dim3(64 * 12), 0, s, a);
   return launch_status();
 }
 

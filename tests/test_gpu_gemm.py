@@ -174,6 +174,43 @@ def test_xcd_banded_tile_order_full_outputs(gpu_lib):
     assert_gemm_parity(got, c64, mag, out_bf16=False, label=f"wgrad banded order {mw}x{nw}x{t}")
 
 
+def test_persistent_tiles_full_outputs(gpu_lib):
+    """Shapes with more 256x128 (or 192x128) tiles than CUs, so each workgroup
+    of the warp-specialized kernel walks several tiles and the LDS ring runs
+    across tile boundaries: forward 8200x1664x1024 (429 tiles), dgrad
+    4173x2304 over 1536 (396 tiles of 192 rows), weight gradient 1100x7204 over 1024
+    tokens (342 tiles of 192 rows).  Ragged M (and N for the weight gradient);
+    NaN-filled outputs compared element by element with the oracle."""
+    rng = np.random.default_rng(212)
+
+    def nan_bf16(m, n):
+        return torch.full((m, n), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+    m, n, k = 8200, 1664, 1024
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, k // 128)), random_scales(rng, (n // 128, k // 128))
+    c = nan_bf16(m, n)
+    gpu_lib.fp8bs_gemm(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), c=c)
+    mag = gemm_fprop(magnitude_codes(qa), sa, magnitude_codes(qb), sb)
+    assert_gemm_parity(bf16_values_host(c), gemm_fprop(qa, sa, qb, sb), mag, label=f"fprop persistent {m}x{n}x{k}")
+    m, kc, ko = 4173, 1536, 2304
+    qd, sd = random_codes(rng, (m, kc)), random_scales(rng, (m, kc // 128))
+    qw, sw = random_codes(rng, (kc, ko)), random_scales(rng, (kc // 128, ko // 128))
+    c = nan_bf16(m, ko)
+    gpu_lib.fp8bs_gemm(to_dev(qd), to_dev(sd), to_dev(qw), to_dev(sw), b_layout=1, c=c)
+    mag = gemm_dgrad(magnitude_codes(qd), sd, magnitude_codes(qw), sw)
+    assert_gemm_parity(bf16_values_host(c), gemm_dgrad(qd, sd, qw, sw), mag, label=f"dgrad persistent {m}x{ko}x{kc}")
+    mw, nw, t = 1100, 7204, 1024
+    qa2, qb2 = random_codes(rng, (mw, t)), random_codes(rng, (nw, t))
+    sa2, sb2 = random_scales(rng, (mw, t // 128)), random_scales(rng, (nw, t // 128))
+    out = torch.full((mw, nw), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_lib.fp8bs_gemm_wgrad(to_dev(qa2), to_dev(sa2), to_dev(qb2), to_dev(sb2), c=out)
+    got = out.cpu().numpy().astype(np.float64)
+    mag = gemm_wgrad(magnitude_codes(qa2), sa2, magnitude_codes(qb2), sb2)
+    assert_gemm_parity(got, gemm_wgrad(qa2, sa2, qb2, sb2), mag, out_bf16=False,
+                       label=f"wgrad persistent {mw}x{nw}x{t}")
+
+
 def test_dgrad_random_codes(gpu_lib):
     rng = np.random.default_rng(202)
     for m, k, n in [(3, 128, 128), (130, 256, 384), (256, 384, 256)]:      # contraction k, output n
