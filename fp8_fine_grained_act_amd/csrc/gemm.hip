@@ -552,16 +552,22 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   // patch.  Tiles: 256 x 128 or 192 x 128 (the launcher picks the height
   // that leaves fewer idle CUs in the last round of tiles), and 128 x 256 for
   // the grouped GEMM, whose expert segments come in 128-row steps.
-  constexpr int WAVES_N = BN / 64;
+  // wave grid: BN / 64 waves across N (patches 64 wide), except 192-wide
+  // tiles: 2 waves of 96 columns (MW = 4) or 4 of 48 (MW = 8)
+  constexpr int WAVES_N = BN == 192 ? (MW == 4 ? 2 : 4) : BN / 64;
   constexpr int WAVES_M = MW / WAVES_N;
-  constexpr int WM = BM / WAVES_M, WN = 64, TM = WM / 16, TN = 4;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 16, TN = WN / 16;
+  // a patch narrower or wider than 64 columns can straddle a 128-column
+  // weight block: then each 16-column MFMA tile takes its own weight scale
+  constexpr bool kWbPerTile = MODE != kWgrad && WN != 64;
   constexpr int A_CP = BM / 8 / 4;            // A copies (8 rows each) per copy wave
   constexpr int B_CP = BN / 8 / 4;            // B copies per copy wave
   constexpr int SA_JOBS = BM / 64;            // 64-row scale copies of A
   constexpr int SB_JOBS = BN / 64;            // 64-column scale copies of B
   static_assert(MODE == kFprop || MODE == kDgrad || MODE == kWgrad || MODE == kGrouped, "mode");
   static_assert(MW == 4 || MW == 8, "MFMA wave count");
-  static_assert((BN == 128 && (BM == 256 || BM == 192)) || (BN == 256 && BM == 128 && MODE != kDgrad),
+  static_assert((BN == 128 && (BM == 256 || BM == 192)) ||
+                    ((BN == 256 || BN == 192) && BM == 128 && MODE != kDgrad),
                 "tile shape");
   static_assert(WAVES_M * WAVES_N == MW && WM % 16 == 0, "whole MFMA tiles per wave");
 
@@ -765,7 +771,8 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     v8i bf[TN];
     v8i a0;
     float wa0;
-    float wb0;      // forward / dgrad: one weight block covers the 128 columns
+    float wb0;      // forward / dgrad: one weight block covers the patch's columns
+    float wbs[TN];  // or one per 16-column MFMA tile (kWbPerTile)
     v4f wb[TN];     // weight gradient: a scale per column
   };
   // reads in the order of first use: B fragment 0 and A fragment 0 (the
@@ -780,9 +787,12 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
       for (int i = 0; i < TN; ++i) h.wb[i] = *reinterpret_cast<const v4f*>(&s.sb[WN * wn + 16 * i + 4 * g]);
       h.wb0 = 0.f;
     } else {
-      h.wb0 = s.sb[WN * wn];
+      h.wb0 = kWbPerTile ? 0.f : s.sb[WN * wn];
 #pragma unroll
-      for (int i = 0; i < TN; ++i) h.wb[i] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < TN; ++i) {
+        h.wbs[i] = kWbPerTile ? s.sb[WN * wn + 16 * i] : 0.f;
+        h.wb[i] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
     }
 #pragma unroll
     for (int i = 1; i < TN; ++i) h.bf[i] = MODE == kDgrad ? frag_b_tr(s.b, i) : frag(s.b, b_lo, b_hi, i);
@@ -791,7 +801,7 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   // LDS instructions of one head, spread over the MFMAs of the group that
   // reads it (issued all at once they queue behind each other and hold up
   // that group's MFMAs)
-  constexpr int kHeadReads = (MODE == kDgrad ? 4 * TN : 2 * TN) + 2 + 1 + (MODE == kWgrad ? TN : 1);
+  constexpr int kHeadReads = (MODE == kDgrad ? 4 * TN : 2 * TN) + 2 + 1 + (MODE == kWgrad || kWbPerTile ? TN : 1);
   constexpr int kHeadPerMfma = (kHeadReads + TN - 1) / TN;
   auto barrier = [&]() {
     asm volatile("" ::: "memory");
@@ -864,7 +874,7 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
         if (t > 0) fold((t - 1) % TN, (t - 1) / TN);
         else fold(TN - 1, TM - 1);
         P_prev = P;
-        pw = wj;
+        pw = kWbPerTile ? wa_cur * hd.wbs[i] : wj;
         if (MODE == kWgrad) pwb = hd.wb[i];
       }
       // per 16-row group: the LDS reads of the next group first, then per
@@ -971,15 +981,39 @@ static int64_t persistent_grid(const GemmArgs& a, int cus) {
 // (one wave's fold and LDS reads issue under the other's MFMAs: forward
 // 4096x1536x7168 61.5 -> 56.7 us); one per SIMD for the weight gradient,
 // whose 8-instruction fold per MFMA does not fit 168 VGPRs without spills.
+template <int MODE, int MW>
+static int launch_wide(GemmArgs a, hipStream_t s, int cus) {
+  a.tiles_n = (a.n + 191) / 192;
+  a.tiles_m = (a.m + 127) / 128;
+  a.group_m = choose_group_m(a, 128, 192, 2);
+  const int64_t tiles = a.tiles_m * a.tiles_n;
+  const int64_t grid = persistent_grid(a, cus);
+  if (grid <= 0) return FP8BS_ERR_SHAPE;
+  if (grid < tiles)
+    hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 128, 192, true>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_ws_kernel<MODE, MW, 128, 192, false>), dim3((unsigned)grid), dim3(64 * (MW + 4)), 0, s, a);
+  return launch_status();
+}
+
+// Tile shape: rounds of one tile per CU times the tile area times the shape's
+// cost per unit of area, smallest wins.  Measured relative costs: 256x128
+// 1.0, 192x128 1.1 (smaller MFMA patches read more LDS per MFMA), 128x192
+// 1.21 (forward only: 64x48 patches; it pays where 256x128 tiles leave CUs
+// idle, forward 4096x1536x7168 56.9 -> 51.7 us).
+static int64_t tile_cost(int64_t m, int64_t n, int bm, int bn, int cost100, int cus) {
+  const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+  return ((tiles + cus - 1) / cus) * bm * bn * cost100;
+}
+
 template <int MODE>
 static int launch_gemm_ws(GemmArgs a, hipStream_t s, int cus) {
   constexpr int MW = MODE == kWgrad ? 4 : 8;
+  const int64_t c256 = tile_cost(a.m, a.n, 256, 128, 100, cus), c192 = tile_cost(a.m, a.n, 192, 128, 110, cus);
+  if (MODE == kFprop && tile_cost(a.m, a.n, 128, 192, 121, cus) < (c256 < c192 ? c256 : c192))
+    return launch_wide<kFprop, 8>(a, s, cus);
   a.tiles_n = (a.n + 127) / 128;
-  // tile height: rounds of one tile per CU times the tile height, smaller
-  // wins; a 192-row tile does ~10% less per cycle (smaller MFMA patches read
-  // more LDS per MFMA), so its cost is weighted by 11/10
-  const int64_t t256 = ((a.m + 255) / 256) * a.tiles_n, t192 = ((a.m + 191) / 192) * a.tiles_n;
-  const bool tall = ((t256 + cus - 1) / cus) * 256 * 10 <= ((t192 + cus - 1) / cus) * 192 * 11;
+  const bool tall = c256 <= c192;
   a.tiles_m = tall ? (a.m + 255) / 256 : (a.m + 191) / 192;
   a.group_m = choose_group_m(a, tall ? 256 : 192, 128, MODE == kWgrad ? 4 : 2);
   const int64_t tiles = a.tiles_m * a.tiles_n;

@@ -211,6 +211,22 @@ def test_persistent_tiles_full_outputs(gpu_lib):
                        label=f"wgrad persistent {mw}x{nw}x{t}")
 
 
+def test_wide_forward_tiles_full_output(gpu_lib):
+    """A forward shape whose 256x128 tiles would leave CUs idle (198 tiles),
+    so the launch takes 128x192 tiles (255 of them): ragged M (2113) and a
+    last tile column 128 wide (2816 = 14 x 192 + 128); the 48-column wave
+    patches straddle 128-column weight blocks, so each 16-column MFMA tile
+    takes its own weight scale."""
+    rng = np.random.default_rng(213)
+    m, n, k = 2113, 2816, 1024
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, k // 128)), random_scales(rng, (n // 128, k // 128))
+    c = torch.full((m, n), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    gpu_lib.fp8bs_gemm(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), c=c)
+    mag = gemm_fprop(magnitude_codes(qa), sa, magnitude_codes(qb), sb)
+    assert_gemm_parity(bf16_values_host(c), gemm_fprop(qa, sa, qb, sb), mag, label=f"fprop wide {m}x{n}x{k}")
+
+
 def test_dgrad_random_codes(gpu_lib):
     rng = np.random.default_rng(202)
     for m, k, n in [(3, 128, 128), (130, 256, 384), (256, 384, 256)]:      # contraction k, output n
