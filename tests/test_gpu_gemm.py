@@ -227,6 +227,33 @@ def test_wide_forward_tiles_full_output(gpu_lib):
     assert_gemm_parity(bf16_values_host(c), gemm_fprop(qa, sa, qb, sb), mag, label=f"fprop wide {m}x{n}x{k}")
 
 
+def test_mid_size_128_tiles_full_outputs(gpu_lib):
+    """Problems with at least one 128x128 tile per CU but too few 256x128 tiles
+    for the warp-specialized kernel run the 128x128 kernel: forward, dgrad and
+    weight gradient at 2048x2048 (ragged M for the forward), every element
+    compared with the oracle."""
+    rng = np.random.default_rng(214)
+    m, n, k = 2000, 2048, 512
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, k // 128)), random_scales(rng, (n // 128, k // 128))
+    got = bf16_values_host(gpu_lib.fp8bs_gemm(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb)))
+    mag = gemm_fprop(magnitude_codes(qa), sa, magnitude_codes(qb), sb)
+    assert_gemm_parity(got, gemm_fprop(qa, sa, qb, sb), mag, label=f"fprop 128 tiles {m}x{n}x{k}")
+    m, kc, ko = 2048, 512, 2048
+    qd, sd = random_codes(rng, (m, kc)), random_scales(rng, (m, kc // 128))
+    qw, sw = random_codes(rng, (kc, ko)), random_scales(rng, (kc // 128, ko // 128))
+    got = bf16_values_host(gpu_lib.fp8bs_gemm(to_dev(qd), to_dev(sd), to_dev(qw), to_dev(sw), b_layout=1))
+    mag = gemm_dgrad(magnitude_codes(qd), sd, magnitude_codes(qw), sw)
+    assert_gemm_parity(got, gemm_dgrad(qd, sd, qw, sw), mag, label=f"dgrad 128 tiles {m}x{ko}x{kc}")
+    mw, nw, t = 2048, 2048, 512
+    qa2, qb2 = random_codes(rng, (mw, t)), random_codes(rng, (nw, t))
+    sa2, sb2 = random_scales(rng, (mw, t // 128)), random_scales(rng, (nw, t // 128))
+    out = gpu_lib.fp8bs_gemm_wgrad(to_dev(qa2), to_dev(sa2), to_dev(qb2), to_dev(sb2))
+    got = out.cpu().numpy().astype(np.float64)
+    mag = gemm_wgrad(magnitude_codes(qa2), sa2, magnitude_codes(qb2), sb2)
+    assert_gemm_parity(got, gemm_wgrad(qa2, sa2, qb2, sb2), mag, out_bf16=False, label=f"wgrad 128 tiles {mw}x{nw}x{t}")
+
+
 def test_dgrad_random_codes(gpu_lib):
     rng = np.random.default_rng(202)
     for m, k, n in [(3, 128, 128), (130, 256, 384), (256, 384, 256)]:      # contraction k, output n
