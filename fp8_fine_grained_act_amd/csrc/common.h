@@ -138,4 +138,38 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// ---- buffer copies straight into LDS, and vmcnt waits ---------------------
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access, gfx9 family
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint32_t nb = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFLL ? 0xFFFFFFFFu : (uint32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nb, kRsrcWord3);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)lds, 4, (int)voff, (int)soff, 0, 0);
+}
+
+// s_waitcnt with only a vmcnt limit (expcnt, lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+// wave-uniform runtime limit: a chain of scalar compares picks the immediate
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n >= N) {
+    wait_vmcnt<N>();
+  } else if constexpr (N > 0) {
+    wait_vmcnt_le<N - 1>(n);
+  }
+}
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) { wait_vmcnt_le<47>(n); }
+
 }  // namespace fp8bs

@@ -104,22 +104,6 @@ __device__ inline TileMN tile_coords(const GemmArgs& p, uint32_t b) {
 }
 
 constexpr int BK = 128;
-constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access, gfx9 family
-
-typedef __attribute__((address_space(3))) void lds_ptr_t;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const uint32_t nb = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFLL ? 0xFFFFFFFFu : (uint32_t)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nb, kRsrcWord3);
-}
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)lds, 16, (int)voff, (int)soff, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)lds, 4, (int)voff, (int)soff, 0, 0);
-}
-
 // LDS bank layout, measured on gfx950 (bank-conflict counter, one lane pair
 // at a time): 64 banks of 4 bytes; ds_read_b128 serves 16 lanes per pass,
 // lanes 0-3, 12-15, 20-23 and 24-27 forming one pass (within each half
@@ -144,22 +128,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chu
 // the same in the dgrad weight layout
 __device__ __forceinline__ int swz_t(int row, int chunk) { return row * BK + ((chunk ^ swz_ht(row)) << 4); }
 
-// s_waitcnt with only a vmcnt limit (expcnt, lgkmcnt left unconstrained)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-// wave-uniform runtime limit: a chain of scalar compares picks the immediate
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  if (n >= N) {
-    wait_vmcnt<N>();
-  } else if constexpr (N > 0) {
-    wait_vmcnt_le<N - 1>(n);
-  }
-}
-__device__ __forceinline__ void wait_vmcnt_dyn(int n) { wait_vmcnt_le<47>(n); }
+
 
 template <int BM, int BN>
 struct Stage {
@@ -1063,17 +1032,6 @@ using namespace fp8bs;
 // fewer such tiles than three quarters of the CUs, the 128 x 128 kernel (two
 // tiles per CU) keeps more of the chip busy.  FP8BS_GEMM_TILE=128|256 forces
 // a choice (experiments and tests of both paths).
-static int cu_count() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 static bool use_ws(int64_t m, int64_t n) {
   static int forced = -1;
   if (forced < 0) {

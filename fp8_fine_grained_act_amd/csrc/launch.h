@@ -20,4 +20,18 @@ inline int launch_status() {
   return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH;
 }
 
+// Compute units of the current device (cached per device; persistent grids
+// and tile-shape choices are sized by it).
+inline int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 }  // namespace fp8bs
