@@ -40,7 +40,6 @@
 //     and odd lanes at the same rows of columns n+8..n+15 leaves lane i with 8
 //     consecutive k of column n + i.
 
-#include <stdlib.h>
 
 #include "common.h"
 #include "launch.h"
@@ -424,7 +423,6 @@ void gemm_kernel(GemmArgs p) {
 // banded order leaves the XCDs writing narrow column windows a fixed stride
 // apart, which measured up to 2x slower on a 4096 x 32768 x 512 forward GEMM
 // (the order changes nothing else for them).
-// FP8BS_GEMM_GROUP_M=<h> forces a height, and -1 the plain order.
 static int64_t range_cost(int64_t tiles_m, int64_t tiles_n, int64_t bm, int64_t bn, int64_t gm) {
   const int64_t tiles = tiles_m * tiles_n;
   const int64_t per = (tiles + kXcds - 1) / kXcds, full = tiles - kXcds * (per - 1);
@@ -448,14 +446,7 @@ static int64_t range_cost(int64_t tiles_m, int64_t tiles_n, int64_t bm, int64_t 
   return cost;
 }
 static int64_t choose_group_m(const GemmArgs& a, int64_t bm, int64_t bn, int64_t out_bytes) {
-  static int forced = -2;
-  if (forced == -2) {
-    const char* e = getenv("FP8BS_GEMM_GROUP_M");
-    forced = e ? atoi(e) : 0;
-  }
   const int64_t tiles_m = a.tiles_m, tiles_n = a.tiles_n;
-  if (forced < 0) return 0;
-  if (forced > 0) return forced < tiles_m ? forced : tiles_m;
   if ((double)a.m * (double)a.n * (double)out_bytes > 2.0 * (double)(a.m + a.n) * (double)a.k) return 0;
   int64_t best = 1, best_cost = -1;
   const int64_t hi = tiles_m < 32 ? tiles_m : 32;
@@ -1027,19 +1018,11 @@ static int launch_grouped_ws(GemmArgs a, hipStream_t s) {
 
 using namespace fp8bs;
 
-// Kernel choice.  The warp-specialized 256 x 128 kernel (gemm_ws_kernel) is
-// the faster one per CU, but it runs one tile per CU; when a problem has
-// fewer such tiles than three quarters of the CUs, the 128 x 128 kernel (two
-// tiles per CU) keeps more of the chip busy.  FP8BS_GEMM_TILE=128|256 forces
-// a choice (experiments and tests of both paths).
+// Kernel choice.  The warp-specialized kernel (gemm_ws_kernel) is the faster
+// one per CU, but it runs one large tile per CU; when a problem has fewer
+// 256 x 128 tiles than three quarters of the CUs, gemm_kernel (smaller tiles,
+// two workgroups per CU) keeps more of the chip busy.
 static bool use_ws(int64_t m, int64_t n) {
-  static int forced = -1;
-  if (forced < 0) {
-    const char* e = getenv("FP8BS_GEMM_TILE");
-    forced = e ? atoi(e) : 0;
-  }
-  if (forced == 128) return false;
-  if (forced == 256) return true;
   const int64_t tiles = ((m + 255) / 256) * ((n + 127) / 128);
   return 4 * tiles >= 3 * cu_count();
 }
