@@ -12,10 +12,13 @@
 // products span many binades); the FP32 promotion bounds how far that error
 // can accumulate, as on the pages' hardware.
 //
-// Two kernels share the slab layout below: gemm_kernel (128 x 128 tiles, every
-// wave both copies and multiplies, two workgroups per CU; also the MoE grouped
-// GEMM) and gemm_ws_kernel (256 x 128 tiles, separate copy and MFMA waves,
-// described above that kernel).
+// Two kernels share the slab layout below: gemm_kernel (128 x 128 or 64 x 128
+// tiles, every wave both copies and multiplies, two workgroups per CU; small
+// and mid-size problems) and gemm_ws_kernel (256 x 128, 192 x 128, 128 x 192
+// and, for the MoE grouped GEMM, 128 x 256 tiles; separate copy and MFMA
+// waves; persistent over tiles where a workgroup gets several; described
+// above that kernel).  The host picks the kernel, tile shape and tile order
+// (use_ws, tile_cost, choose_group_m).
 //
 // Structure of one gemm_kernel workgroup (WAVES_M x WAVES_N waves, each wave a
 // (BM/WAVES_M) x (BN/WAVES_N) patch of 16x16 MFMA tiles):
@@ -39,7 +42,6 @@
 //     b = 0..7; pointing even lanes at 8 consecutive k rows of columns n..n+7
 //     and odd lanes at the same rows of columns n+8..n+15 leaves lane i with 8
 //     consecutive k of column n + i.
-
 
 #include "common.h"
 #include "launch.h"
@@ -475,7 +477,7 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Warp-specialized 256 x 128 tile: 4 MFMA waves + 4 copy waves.
+// Warp-specialized tiles: MW MFMA waves (4 or 8) + 4 copy waves.
 //
 // Measured on gfx950: a copy of 1 KB (buffer_load ... lds or a plain vector
 // load) holds its wave for ~70-100 issue cycles, so a wave that both copies
@@ -483,9 +485,8 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // idles while the waves of a workgroup copy in lockstep.  The MFMAs of one
 // wave per SIMD, on the other hand, run at the full rate (one 16x16x128 FP8
 // MFMA per 32 cycles) while another wave on the same SIMD copies, loads or
-// reads LDS.  So the roles are split: waves 0-3 (one per SIMD) only read
-// fragments and run MFMAs and the per-slab rescale, each on a 128 x 64 patch
-// (8 x 4 tiles of 16 x 16, accumulators 128 VGPRs); waves 4-7 only copy
+// reads LDS.  So the roles are split: the MFMA waves only read fragments and
+// run MFMAs and the per-block fold; the last 4 waves (one per SIMD) only copy
 // slabs into a 3-deep LDS ring (each stage its own LDS object, so the
 // compiler sees that a copy never touches the slab being read).
 //
@@ -506,14 +507,13 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 template <int MODE, int MW, int BM, int BN, bool PERSIST>
 __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
-  // MW MFMA waves: 4 (one per SIMD) or 8 (two per SIMD, so one wave's
-  // rescale VALU work runs under the other's MFMAs; register budget 168 per
-  // lane for three waves per SIMD), BN / 64 of them across N, each a WM x 64
-  // patch.  Tiles: 256 x 128 or 192 x 128 (the launcher picks the height
-  // that leaves fewer idle CUs in the last round of tiles), and 128 x 256 for
-  // the grouped GEMM, whose expert segments come in 128-row steps.
-  // wave grid: BN / 64 waves across N (patches 64 wide), except 192-wide
-  // tiles: 2 waves of 96 columns (MW = 4) or 4 of 48 (MW = 8)
+  // MW MFMA waves: 4 (one per SIMD) or 8 (two per SIMD, so one wave's fold
+  // VALU work runs under the other's MFMAs; register budget 168 per lane for
+  // three waves per SIMD).  Tiles: 256 x 128 or 192 x 128 (launcher's choice,
+  // tile_cost), 128 x 192 for forward GEMMs whose larger tiles leave CUs idle,
+  // and 128 x 256 for the grouped GEMM, whose expert segments come in 128-row
+  // steps.  Wave grid: BN / 64 waves across N (patches 64 wide), except
+  // 192-wide tiles: 2 waves of 96 columns (MW = 4) or 4 of 48 (MW = 8).
   constexpr int WAVES_N = BN == 192 ? (MW == 4 ? 2 : 4) : BN / 64;
   constexpr int WAVES_M = MW / WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 16, TN = WN / 16;
