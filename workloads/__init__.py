@@ -1,8 +1,8 @@
 """Seeded synthetic workloads shared by the tests, the smoke check and the benchmark.
 
 This module holds no part of the FP8 method: it only draws random bf16 inputs
-(and the MoE routing counts) of the shapes and value distributions of the
-benchmark configurations.  Both the CPU oracle and the HIP library are fed
+(and the MoE routing: top-k expert ids, gate weights, counts) of the shapes
+and value distributions of the benchmark configurations.  Both the CPU oracle and the HIP library are fed
 from here; neither imports the other.
 
 Shapes follow the pages' model: hidden size 7168, MLA query latent 1536 and
@@ -30,6 +30,7 @@ from .gen import (
     layer_inputs,
     wgrad_inputs,
     moe_routing,
+    moe_dispatch_inputs,
     grouped_inputs_host,
     device_expert_weights,
     normal_bf16,
@@ -37,5 +38,5 @@ from .gen import (
 
 __all__ = [
     "CONFIGS", "config_by_name", "f32_to_bf16_bits", "gemm_inputs", "layer_inputs", "wgrad_inputs",
-    "moe_routing", "grouped_inputs_host", "device_expert_weights", "normal_bf16",
+    "moe_routing", "moe_dispatch_inputs", "grouped_inputs_host", "device_expert_weights", "normal_bf16",
 ]

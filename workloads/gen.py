@@ -91,6 +91,43 @@ def wgrad_inputs(name_or_cfg, **override):
     return dict(dy=dy_bits, x=x_bits, outlier_rows=rows)
 
 
+def _topk_choice(cfg):
+    """Seeded top-k expert choice: (ids [T, k] by descending key, keys [T, E], rng).
+
+    Expert e has popularity p(e) proportional to (e+1)^(-s); a token's k
+    distinct experts come from the Gumbel-top-k trick on log p (one Gumbel
+    draw per token and expert), listed from the largest key down.
+    """
+    tokens, topk, num_e, s = cfg["tokens"], cfg["topk"], cfg["experts"], cfg["zipf_s"]
+    rng = _streams(cfg["seed"])[3]
+    logp = -s * np.log(np.arange(1, num_e + 1, dtype=np.float64))
+    keys = logp[None, :] + rng.gumbel(size=(tokens, num_e))
+    chosen = np.argpartition(-keys, topk - 1, axis=1)[:, :topk]
+    order = np.argsort(-np.take_along_axis(keys, chosen, axis=1), axis=1, kind="stable")
+    return np.take_along_axis(chosen, order, axis=1), keys, rng
+
+
+def moe_dispatch_inputs(name_or_cfg, hidden=None, **override):
+    """Token-order inputs of the MoE dispatch and combine.
+
+    ids    int32 [T, k]   top-k expert ids (``_topk_choice``)
+    gates  float32 [T, k] gate weights: uniform(0.05, 1) draws, divided by
+           their per-token sum (positive, summing to about 1, like normalized
+           router affinities of the chosen experts)
+    x      bf16 bits [T, hidden] i.i.d. N(0, a_std) token activations
+    hidden defaults to the configuration's K (the model width).
+    """
+    cfg = config_by_name(name_or_cfg) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
+    cfg.update(override)
+    ids, _, rng = _topk_choice(cfg)
+    tokens, topk = ids.shape
+    g = rng.uniform(0.05, 1.0, size=(tokens, topk)).astype(np.float32)
+    g /= g.sum(axis=1, keepdims=True, dtype=np.float32)
+    h = int(cfg["K"] if hidden is None else hidden)
+    x = normal_bf16(_streams(cfg["seed"])[0], (tokens, h), cfg.get("a_std", 1.0))
+    return dict(ids=ids.astype(np.int32), gates=g.astype(np.float32), x=x, experts=int(cfg["experts"]))
+
+
 def moe_routing(name_or_cfg, **override):
     """Per-expert routed-row counts for top-k routing with Zipf-skewed popularity.
 
@@ -102,10 +139,7 @@ def moe_routing(name_or_cfg, **override):
     cfg = config_by_name(name_or_cfg) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
     cfg.update(override)
     tokens, topk, num_e, s = cfg["tokens"], cfg["topk"], cfg["experts"], cfg["zipf_s"]
-    rng = _streams(cfg["seed"])[3]
-    logp = -s * np.log(np.arange(1, num_e + 1, dtype=np.float64))
-    keys = logp[None, :] + rng.gumbel(size=(tokens, num_e))
-    chosen = np.argpartition(-keys, topk - 1, axis=1)[:, :topk]
+    chosen = _topk_choice(cfg)[0]
     counts = np.bincount(chosen.ravel(), minlength=num_e).astype(np.int64)
     padded = (counts + GROUP - 1) // GROUP * GROUP
     offsets = np.zeros(num_e + 1, dtype=np.int64)
