@@ -191,6 +191,11 @@ void gemm_kernel(GemmArgs p) {
   const int64_t M = p.m, N = p.n, K = p.k;
   const int nkb = (int)(K / BK);
 
+  // grouped: a tile at or past the end of the last segment holds no expert's
+  // rows (the row capacity can exceed the padded total); the workgroup leaves
+  // before its first barrier and writes nothing
+  if (MODE == kGrouped && m0 >= (int64_t)p.seg[p.num_experts]) return;
+
   const uint8_t* qb = p.qb;
   const float* sb = p.sb;
   if (MODE == kGrouped) {
@@ -562,6 +567,12 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     const TileMN t = tile_coords(p, (uint32_t)((int64_t)blockIdx.x + (int64_t)i * G));
     return Origin{(int64_t)t.m * BM, (int64_t)t.n * BN};
   };
+
+  // grouped: a tile at or past the end of the last segment holds no expert's
+  // rows (the row capacity can exceed the padded total); the whole workgroup
+  // leaves before its first barrier and writes nothing
+  static_assert(!(MODE == kGrouped && PERSIST), "grouped tiles are one per workgroup");
+  if (MODE == kGrouped && tile_origin(0).m0 >= (int64_t)p.seg[p.num_experts]) return;
 
   if (wave >= MW) {
     // ======================= copy waves ==========================================

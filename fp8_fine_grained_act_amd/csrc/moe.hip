@@ -1,0 +1,339 @@
+// MoE dispatch and combine around the grouped GEMM (gfx950).
+//
+// Each token is routed to k of the routed experts (deepseek.csdn.net page,
+// section 一(二) "DeepSeekMoE 架构"); a layer's chunk dispatches the tokens to
+// their experts before the expert MLP and combines the expert outputs after it
+// (qqstock.cn page, section "DualPipe 流水線并行"); activations travel in FP8
+// and the combined outputs in BF16 (deepseek.csdn.net page, section 二(四)).
+// On one GPU the dispatch is a permutation into expert-major rows, each
+// expert's run padded to a multiple of 128 rows so that every 128-row tile of
+// the grouped GEMM belongs to one expert.
+//
+//   moe_route_kernel     one workgroup: a stable counting sort of the
+//                        (token, slot) pairs by expert id, giving the padded
+//                        segment starts, each pair's row and each row's token
+//   moe_dispatch_kernel  each token row is read once, coded once in 1x128
+//                        tiles and its codes and scales stored to its k rows;
+//                        one workgroup per expert zeroes its padding rows
+//   moe_combine_kernel   one wave per token: the gate-weighted FP32 sum of the
+//                        token's k expert-output rows, rounded once to bf16
+//
+// Nothing here reads a size from the device to size a launch: the grids come
+// from host sizes and the largest padded row count, so the three calls and the
+// grouped GEMM between them need no host synchronization.  Every row index
+// that comes from device memory is checked against the row capacity before it
+// is used, so no device contents can make a kernel access memory outside the
+// caller's buffers.
+
+#include "common.h"
+#include "launch.h"
+
+namespace fp8bs {
+
+constexpr int kRouteWaves = 16;            // one 1024-thread workgroup
+constexpr int kRouteMaxExperts = 1024;
+constexpr int kMaxTopk = 64;               // a token's slots fit in one wave's lanes
+
+// ---------------------------------------------------------------------------
+// Routing: wave w owns the pairs [lo_w, hi_w) (pairs in row-major
+// (token, slot) order, chunks in wave order), so "earlier pair" means an
+// earlier wave, or an earlier 64-pair step of the same wave, or a lower lane.
+//   1. per-wave histograms in LDS (atomic adds: counts do not depend on order)
+//   2. per expert: exclusive prefix over the waves, count, padded size; an
+//      exclusive scan of the padded sizes over the experts gives the segment
+//      starts; each wave's running row for expert e = start + its prefix
+//   3. each wave walks its chunk 64 pairs at a time: lanes holding the same
+//      expert are found with one ballot per id bit, a pair's rank among them is
+//      the population count of the matching lower lanes, and the lowest such
+//      lane advances the running row by the group's size
+//   4. rows of padding (and rows past the padded total) get token -1
+__global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restrict__ ids, int64_t pairs,
+                                                         int topk, int num_e, int id_bits,
+                                                         int32_t* __restrict__ seg,
+                                                         int32_t* __restrict__ slot_rows,
+                                                         int32_t* __restrict__ row_token, int64_t cap) {
+  __shared__ int next_row[kRouteWaves][kRouteMaxExperts];
+  __shared__ int seg_s[kRouteMaxExperts + 1];
+  __shared__ int cnt_s[kRouteMaxExperts];
+  __shared__ int wave_sum[kRouteWaves];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  if (tid < num_e)
+    for (int v = 0; v < kRouteWaves; ++v) next_row[v][tid] = 0;
+  __syncthreads();
+
+  const int64_t chunk = ((pairs + kRouteWaves - 1) / kRouteWaves + 63) / 64 * 64;
+  const int64_t lo = min(pairs, (int64_t)w * chunk), hi = min(pairs, lo + chunk);
+  for (int64_t i = lo + lane; i < hi; i += 64) {
+    const int e = ids[i];
+    if (e >= 0 && e < num_e) atomicAdd(&next_row[w][e], 1);
+  }
+  __syncthreads();
+
+  int padded = 0;
+  if (tid < num_e) {
+    int run = 0;
+    for (int v = 0; v < kRouteWaves; ++v) {
+      const int c = next_row[v][tid];
+      next_row[v][tid] = run;
+      run += c;
+    }
+    cnt_s[tid] = run;
+    padded = (run + 127) & ~127;
+  }
+  int incl = padded;                                   // inclusive scan inside the wave
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_sum[w] = incl;
+  __syncthreads();
+  int excl = incl - padded;
+  for (int v = 0; v < w; ++v) excl += wave_sum[v];
+  if (tid < num_e) {
+    seg_s[tid] = excl;
+    seg[tid] = excl;
+    for (int v = 0; v < kRouteWaves; ++v) next_row[v][tid] += excl;
+    if (tid == num_e - 1) {
+      seg_s[num_e] = excl + padded;
+      seg[num_e] = excl + padded;
+    }
+  }
+  __syncthreads();
+
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t i0 = lo; i0 < hi; i0 += 64) {
+    const int64_t i = i0 + lane;
+    const bool in = i < hi;
+    const int e = in ? ids[i] : -1;
+    const bool ok = in && e >= 0 && e < num_e;
+    uint64_t same = __ballot(ok);
+    for (int b = 0; b < id_bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t on = __ballot(ok && bit);
+      same &= bit ? on : ~on;
+    }
+    if (ok) {
+      const int rank = __popcll(same & below);
+      const int row = next_row[w][e] + rank;
+      slot_rows[i] = row;
+      row_token[row] = (int)(i / topk);
+      if (rank == 0) next_row[w][e] = row + __popcll(same);
+    } else if (in) {
+      slot_rows[i] = -1;
+    }
+  }
+
+  if (tid < num_e)
+    for (int r = seg_s[tid] + cnt_s[tid]; r < seg_s[tid + 1]; ++r) row_token[r] = -1;
+  for (int64_t r = (int64_t)seg_s[num_e] + tid; r < cap; r += 1024) row_token[r] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch payload.  Token blocks: 4 waves, one token per wave; 8 lanes per
+// 128-element tile (16 bf16 each, two 16-byte loads), so one wave step covers
+// 8 tiles (2 KB of the row) and stores 8 x 1 KB of codes, one full 1 KB run
+// per destination row and store instruction.  The tile's amax, scale and codes
+// are computed exactly as by the 1x128 activation quantizer (a tile depends
+// only on its own 128 values), once per token, whatever k is.
+// Padding blocks (blockIdx.x >= token_blocks): expert e's padding rows lie in
+// the last 128 rows of its segment; each such row whose token is -1 gets +0
+// codes and scale 0.
+__device__ __forceinline__ uint32_t tile16_amax(const uint32_t in[8]) {
+  constexpr uint32_t kMag = 0x7FFF7FFFu;
+  const uint32_t m2 = max_u16x2(max_u16x2(max_u16x2(in[0] & kMag, in[1] & kMag), max_u16x2(in[2] & kMag, in[3] & kMag)),
+                                max_u16x2(max_u16x2(in[4] & kMag, in[5] & kMag), max_u16x2(in[6] & kMag, in[7] & kMag)));
+  return max8_u32(max(m2 & 0xFFFFu, m2 >> 16));
+}
+
+__global__ __launch_bounds__(256) void moe_dispatch_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t tokens, int hidden,
+    const int32_t* __restrict__ slot_rows, int topk, const int32_t* __restrict__ seg,
+    const int32_t* __restrict__ row_token, uint8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ scales, int64_t cap, int64_t token_blocks) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int groups = hidden / kGroup;
+  if ((int64_t)blockIdx.x < token_blocks) {
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= tokens) return;
+    int my_row = -1;                                   // lane j < topk: the row of slot j
+    if (lane < topk) {
+      const int r = slot_rows[t * topk + lane];
+      my_row = (r >= 0 && r < cap) ? r : -1;
+    }
+    const int sg = lane & 7;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + t * ldx + 16 * sg);   // 16 uint4 per tile
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    uint4 a = zero, b = zero;
+    if ((lane >> 3) < groups) {
+      a = xr[16 * (lane >> 3)];
+      b = xr[16 * (lane >> 3) + 1];
+    }
+    for (int g0 = 0; g0 < groups; g0 += 8) {
+      const int g = g0 + (lane >> 3);
+      uint4 na = zero, nb = zero;                      // next step's loads first
+      if (g + 8 < groups) {
+        na = xr[16 * (g + 8)];
+        nb = xr[16 * (g + 8) + 1];
+      }
+      const uint32_t in[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const GroupScale gs = group_scale(tile16_amax(in));
+      uint4 o;
+      quant_run<8>(in, reinterpret_cast<uint32_t*>(&o), gs);
+      for (int j = 0; j < topk; ++j) {                // uniform loop: readlane sees every lane
+        const int row = __builtin_amdgcn_readlane(my_row, j);
+        if (row < 0 || g >= groups) continue;
+        *reinterpret_cast<uint4*>(q + (int64_t)row * ldq + (int64_t)g * kGroup + 16 * sg) = o;
+        if (sg == 0) scales[(int64_t)row * groups + g] = gs.s;
+      }
+      a = na;
+      b = nb;
+    }
+  } else {
+    const int64_t e = (int64_t)blockIdx.x - token_blocks;
+    int64_t hi = seg[e + 1];
+    if (hi > cap) hi = cap;
+    int64_t lo = seg[e];
+    if (lo < hi - kGroup) lo = hi - kGroup;
+    if (lo < 0) lo = 0;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    for (int64_t r = lo + wave; r < hi; r += 4) {
+      if (row_token[r] >= 0) continue;
+      uint8_t* qr = q + r * ldq;
+      for (int c = 16 * lane; c < hidden; c += 1024) *reinterpret_cast<uint4*>(qr + c) = zero;
+      for (int c = lane; c < groups; c += 64) scales[r * groups + c] = 0.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: one wave per token, 8 bf16 columns per lane and step (512 columns
+// per wave step).  The k rows' 16-byte pieces are loaded together, 8 slots
+// at a time, then folded in slot order: acc = fma(g_j, y_j, acc) in FP32,
+// starting from +0; a dropped slot (row -1 or outside the capacity) is
+// skipped.  The sum is rounded once to bf16 (nearest, ties to even).
+__global__ __launch_bounds__(256) void moe_combine_kernel(
+    const uint16_t* __restrict__ y, int64_t ldy, int64_t cap, const int32_t* __restrict__ slot_rows,
+    const float* __restrict__ gates, int64_t tokens, int topk, int n, uint16_t* __restrict__ out,
+    int64_t ldo) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= tokens) return;
+  int my_row = -1;
+  float my_g = 0.0f;
+  if (lane < topk) {
+    const int r = slot_rows[t * topk + lane];
+    my_row = (r >= 0 && r < cap) ? r : -1;
+    my_g = gates[t * topk + lane];
+  }
+  for (int c0 = 0; c0 < n; c0 += 512) {              // uniform loop: readlane sees every lane
+    const int c = c0 + 8 * lane;
+    const bool live = c < n;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j0 = 0; j0 < topk; j0 += 8) {
+      uint4 v[8];
+      int rows[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        rows[jj] = j0 + jj < topk ? __builtin_amdgcn_readlane(my_row, j0 + jj) : -1;
+        v[jj] = rows[jj] >= 0 && live ? *reinterpret_cast<const uint4*>(y + (int64_t)rows[jj] * ldy + c)
+                                      : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (rows[jj] < 0) continue;
+        const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), j0 + jj));
+        const uint32_t d[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = __builtin_fmaf(g, bf16_lo(d[i]), acc[2 * i]);
+          acc[2 * i + 1] = __builtin_fmaf(g, bf16_hi(d[i]), acc[2 * i + 1]);
+        }
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+    o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+    if (live) *reinterpret_cast<uint4*>(out + t * ldo + c) = o;
+  }
+}
+
+static int64_t max_rows(int64_t tokens, int64_t topk, int64_t num_e) {
+  const int64_t pairs = tokens * topk;
+  const int64_t busy = num_e < pairs ? num_e : pairs;
+  return (pairs + 127 * busy) / kGroup * kGroup;
+}
+
+static bool route_sizes_ok(int64_t tokens, int64_t topk, int64_t num_e) {
+  return tokens >= 0 && topk >= 1 && topk <= kMaxTopk && num_e >= 1 && num_e <= 65536 &&
+         tokens <= 0x7FFFFFFFLL / topk && max_rows(tokens, topk, num_e) <= 0x7FFFFFFFLL;
+}
+
+}  // namespace fp8bs
+
+using namespace fp8bs;
+
+extern "C" int64_t fp8bs_moe_max_rows(int64_t tokens, int64_t topk, int64_t num_experts) {
+  if (!route_sizes_ok(tokens, topk, num_experts)) return FP8BS_ERR_SHAPE;
+  return max_rows(tokens, topk, num_experts);
+}
+
+extern "C" int fp8bs_moe_route(const int32_t* topk_ids, int64_t tokens, int64_t topk, int64_t num_experts,
+                               int32_t* seg_offsets, int32_t* slot_rows, int32_t* row_token, int64_t rows_cap,
+                               void* stream) {
+  if (!seg_offsets || (tokens > 0 && (!topk_ids || !slot_rows)) || (rows_cap > 0 && !row_token))
+    return FP8BS_ERR_NULL;
+  if (!route_sizes_ok(tokens, topk, num_experts) || num_experts > kRouteMaxExperts) return FP8BS_ERR_SHAPE;
+  if (rows_cap < max_rows(tokens, topk, num_experts) || rows_cap > 0x7FFFFFFFLL) return FP8BS_ERR_SHAPE;
+  if (!aligned(topk_ids, 4) || !aligned(seg_offsets, 4) || !aligned(slot_rows, 4) || !aligned(row_token, 4))
+    return FP8BS_ERR_ALIGN;
+  int bits = 0;
+  while ((1LL << bits) < num_experts) ++bits;
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(64 * kRouteWaves), 0, (hipStream_t)stream, topk_ids,
+                     tokens * topk, (int)topk, (int)num_experts, bits, seg_offsets, slot_rows, row_token,
+                     rows_cap);
+  return launch_status();
+}
+
+extern "C" int fp8bs_moe_permute_quantize(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t ldx,
+                                          const int32_t* slot_rows, int64_t topk, const int32_t* seg_offsets,
+                                          const int32_t* row_token, int64_t num_experts, uint8_t* q,
+                                          int64_t ldq, float* scales, int64_t rows_cap, void* stream) {
+  if (!seg_offsets || (tokens > 0 && (!x || !slot_rows)) || (rows_cap > 0 && (!row_token || !q || !scales)))
+    return FP8BS_ERR_NULL;
+  if (!route_sizes_ok(tokens, topk, num_experts)) return FP8BS_ERR_SHAPE;
+  if (hidden <= 0 || hidden % kGroup || hidden > (1 << 30) || ldx < hidden || ldq < hidden) return FP8BS_ERR_SHAPE;
+  if (rows_cap < 0 || rows_cap > 0x7FFFFFFFLL) return FP8BS_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4) || !aligned(slot_rows, 4) ||
+      !aligned(seg_offsets, 4) || !aligned(row_token, 4) || ldx % 8 || ldq % 16)
+    return FP8BS_ERR_ALIGN;
+  const int64_t token_blocks = (tokens + 3) / 4;
+  const int64_t grid = token_blocks + num_experts;
+  if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
+  hipLaunchKernelGGL(moe_dispatch_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, x, ldx,
+                     tokens, (int)hidden, slot_rows, (int)topk, seg_offsets, row_token, q, ldq, scales, rows_cap,
+                     token_blocks);
+  return launch_status();
+}
+
+extern "C" int fp8bs_moe_combine(const uint16_t* y, int64_t ldy, int64_t rows_cap, const int32_t* slot_rows,
+                                 const float* gates, int64_t tokens, int64_t topk, int64_t n, uint16_t* out,
+                                 int64_t ldo, void* stream) {
+  if ((rows_cap > 0 && !y) || (tokens > 0 && (!slot_rows || !gates || !out))) return FP8BS_ERR_NULL;
+  if (tokens < 0 || topk < 1 || topk > kMaxTopk || tokens > 0x7FFFFFFFLL / topk) return FP8BS_ERR_SHAPE;
+  if (n <= 0 || n % 8 || n > (1 << 30) || ldy < n || ldo < n || rows_cap < 0 || rows_cap > 0x7FFFFFFFLL)
+    return FP8BS_ERR_SHAPE;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(slot_rows, 4) || !aligned(gates, 4) || ldy % 8 ||
+      ldo % 8)
+    return FP8BS_ERR_ALIGN;
+  if (tokens == 0) return FP8BS_OK;
+  const int64_t grid = (tokens + 3) / 4;
+  if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, y, ldy,
+                     rows_cap, slot_rows, gates, tokens, (int)topk, (int)n, out, ldo);
+  return launch_status();
+}

@@ -31,6 +31,11 @@ _SIGNATURES = {
                            _c_void_p, _c_void_p],
     "fp8bs_gemm_wgrad": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _int,
                          _c_void_p],
+    "fp8bs_moe_route": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p],
+    "fp8bs_moe_permute_quantize": [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _i64,
+                                   _c_void_p, _i64, _c_void_p, _i64, _c_void_p],
+    "fp8bs_moe_combine": [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64,
+                          _c_void_p],
 }
 
 
@@ -52,11 +57,13 @@ def _load():
         fn.restype = ctypes.c_int
     lib.fp8bs_status_string.argtypes = [ctypes.c_int]
     lib.fp8bs_status_string.restype = ctypes.c_char_p
+    lib.fp8bs_moe_max_rows.argtypes = [_i64, _i64, _i64]
+    lib.fp8bs_moe_max_rows.restype = ctypes.c_int64
     return lib
 
 
 raw = _load()
-EXPORTED = tuple(_SIGNATURES) + ("fp8bs_status_string",)
+EXPORTED = tuple(_SIGNATURES) + ("fp8bs_status_string", "fp8bs_moe_max_rows")
 
 
 def status_string(status):
@@ -233,3 +240,95 @@ def fp8bs_gemm_wgrad(qa, sa, qb, sb, c=None, accumulate=0, stream=None):
                               c.data_ptr(), ldc, int(accumulate), _stream(stream))
     _check("fp8bs_gemm_wgrad", st)
     return c
+
+
+def fp8bs_moe_max_rows(tokens, topk, num_experts):
+    """Largest padded row count of the expert-major layout (host only)."""
+    r = raw.fp8bs_moe_max_rows(int(tokens), int(topk), int(num_experts))
+    if r < 0:
+        raise Fp8bsError("fp8bs_moe_max_rows", r)
+    return int(r)
+
+
+def _contig(t, dtype, name):
+    _dev(t, dtype, name)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def fp8bs_moe_route(topk_ids, num_experts, rows_cap=None, seg_offsets=None, slot_rows=None, row_token=None,
+                    stream=None):
+    """Expert-major padded layout of top-k routing: (seg_offsets [E+1], slot_rows [T, k], row_token [cap])."""
+    _contig(topk_ids, torch.int32, "topk_ids")
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [tokens, topk]")
+    tokens, topk = topk_ids.shape
+    if rows_cap is None:
+        rows_cap = fp8bs_moe_max_rows(tokens, topk, num_experts)
+    dev = topk_ids.device
+    if seg_offsets is None:
+        seg_offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    if slot_rows is None:
+        slot_rows = torch.empty((tokens, topk), dtype=torch.int32, device=dev)
+    if row_token is None:
+        row_token = torch.empty(rows_cap, dtype=torch.int32, device=dev)
+    for t, nm in ((seg_offsets, "seg_offsets"), (slot_rows, "slot_rows"), (row_token, "row_token")):
+        _contig(t, torch.int32, nm)
+    if seg_offsets.numel() != num_experts + 1 or tuple(slot_rows.shape) != (tokens, topk) \
+            or row_token.numel() != rows_cap:
+        raise ValueError("output shapes do not match the routing")
+    st = raw.fp8bs_moe_route(topk_ids.data_ptr(), tokens, topk, num_experts, seg_offsets.data_ptr(),
+                             slot_rows.data_ptr(), row_token.data_ptr(), rows_cap, _stream(stream))
+    _check("fp8bs_moe_route", st)
+    return seg_offsets, slot_rows, row_token
+
+
+def fp8bs_moe_permute_quantize(x, slot_rows, seg_offsets, row_token, q=None, scales=None, stream=None):
+    """Dispatch payload: q uint8 [cap, hidden], scales f32 [cap, hidden/128] in expert-major rows."""
+    _dev(x, torch.bfloat16, "x")
+    ldx = _row_major(x, "x")
+    tokens, hidden = x.shape
+    for t, nm in ((slot_rows, "slot_rows"), (seg_offsets, "seg_offsets"), (row_token, "row_token")):
+        _contig(t, torch.int32, nm)
+    if slot_rows.dim() != 2 or slot_rows.shape[0] != tokens:
+        raise ValueError("slot_rows must be [tokens, topk]")
+    topk = slot_rows.shape[1]
+    cap = row_token.numel()
+    num_e = seg_offsets.numel() - 1
+    if q is None:
+        q = torch.empty((cap, hidden), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((cap, hidden // GROUP), dtype=torch.float32, device=x.device)
+    _dev(q, torch.uint8, "q")
+    ldq = _row_major(q, "q")
+    _contig(scales, torch.float32, "scales")
+    if tuple(q.shape) != (cap, hidden) or tuple(scales.shape) != (cap, hidden // GROUP):
+        raise ValueError("output shapes do not match the row capacity")
+    st = raw.fp8bs_moe_permute_quantize(x.data_ptr(), tokens, hidden, ldx, slot_rows.data_ptr(), topk,
+                                        seg_offsets.data_ptr(), row_token.data_ptr(), num_e, q.data_ptr(), ldq,
+                                        scales.data_ptr(), cap, _stream(stream))
+    _check("fp8bs_moe_permute_quantize", st)
+    return q, scales
+
+
+def fp8bs_moe_combine(y, slot_rows, gates, out=None, stream=None):
+    """bf16 out [tokens, n] = sum_j gates[t, j] * y[slot_rows[t, j]] (FP32 accumulation)."""
+    _dev(y, torch.bfloat16, "y")
+    ldy = _row_major(y, "y")
+    cap, n = y.shape
+    _contig(slot_rows, torch.int32, "slot_rows")
+    _contig(gates, torch.float32, "gates")
+    if slot_rows.dim() != 2 or tuple(gates.shape) != tuple(slot_rows.shape):
+        raise ValueError("slot_rows and gates must both be [tokens, topk]")
+    tokens, topk = slot_rows.shape
+    if out is None:
+        out = torch.empty((tokens, n), dtype=torch.bfloat16, device=y.device)
+    _dev(out, torch.bfloat16, "out")
+    ldo = _row_major(out, "out")
+    if tuple(out.shape) != (tokens, n):
+        raise ValueError("out must be [tokens, n]")
+    st = raw.fp8bs_moe_combine(y.data_ptr(), ldy, cap, slot_rows.data_ptr(), gates.data_ptr(), tokens, topk, n,
+                               out.data_ptr(), ldo, _stream(stream))
+    _check("fp8bs_moe_combine", st)
+    return out

@@ -139,7 +139,11 @@ int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const floa
  *   total_rows % 128 == 0, n % 128 == 0, k % 128 == 0, 1 <= num_experts <= 65536.
  * Preconditions on seg_offsets (not checked: they live on the device):
  * seg_offsets[0] == 0, non-decreasing, every entry a multiple of 128,
- * seg_offsets[num_experts] == total_rows.  Empty segments are allowed.
+ * seg_offsets[num_experts] <= total_rows.  Empty segments are allowed.
+ * Rows from seg_offsets[num_experts] to total_rows belong to no expert: their
+ * 128-row tiles end at once and those rows of c are not written (total_rows
+ * may be a capacity such as fp8bs_moe_max_rows, so that no host
+ * synchronization is needed to learn the padded total).
  * Padding rows (rows of a segment beyond the expert's routed rows) are
  * expected to hold zeros in the bf16 source, so their codes and scales are
  * zero and their outputs are exactly 0.
@@ -162,6 +166,90 @@ int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int32_t* seg_of
 int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
                      int64_t m, int64_t n, int64_t t, float* c, int64_t ldc, int accumulate,
                      void* stream);
+
+/*
+ * ---- MoE dispatch and combine around the grouped GEMM ----------------------
+ * Each token is routed to topk of the routed experts (deepseek.csdn.net page,
+ * section 一(二) "DeepSeekMoE 架构": 8 of 256); a layer's chunk dispatches the
+ * tokens to their experts before the expert MLP and combines the expert
+ * outputs after it (qqstock.cn page, section "DualPipe 流水線并行"); the
+ * dispatched activations travel in FP8, the combined outputs in BF16
+ * (deepseek.csdn.net page, section 二(四) "FP8 低精度训练").
+ *
+ * Layout (a reading; the pages do not fix it): expert-major rows.  The
+ * (token, slot) pairs that chose expert e take consecutive rows in
+ * (token, slot) order, starting at seg_offsets[e]; each expert's run is
+ * padded with zero rows up to a multiple of 128, so each 128-row tile of
+ * fp8bs_grouped_gemm belongs to one expert.  A pair whose expert id is
+ * outside [0, num_experts) is dropped: slot row -1, no row, no contribution
+ * to the combine.  slot_rows [tokens, topk] and row_token [rows_cap] are the
+ * two directions of the map.  Routing -> dispatch -> grouped GEMM -> combine
+ * runs with no host synchronization: every buffer is sized by
+ * fp8bs_moe_max_rows.  A pointer may be NULL only when its buffer has no
+ * elements (no tokens, or a zero row capacity).
+ */
+
+/*
+ * Largest padded row count any routing of tokens x topk pairs over
+ * num_experts experts can need: (P + 127 * min(num_experts, P)) rounded down
+ * to a multiple of 128, P = tokens * topk.  Host only.  Returns
+ * FP8BS_ERR_SHAPE (negative) unless tokens >= 0, 1 <= topk <= 64,
+ * 1 <= num_experts <= 65536 and the result fits in int32.
+ */
+int64_t fp8bs_moe_max_rows(int64_t tokens, int64_t topk, int64_t num_experts);
+
+/*
+ * Routing layout on the device (one workgroup; a stable counting sort).
+ *   topk_ids     int32 [tokens, topk]  expert of each (token, slot) pair
+ *   seg_offsets  int32 [num_experts + 1] out: padded segment starts,
+ *                seg_offsets[num_experts] = padded total
+ *   slot_rows    int32 [tokens, topk]  out: row of each pair (-1: dropped id)
+ *   row_token    int32 [rows_cap]      out: token of each row; -1 for padding
+ *                rows and for every row from the padded total to rows_cap
+ *   1 <= num_experts <= 1024, 1 <= topk <= 64, tokens >= 0 (0: all segments
+ *   empty), rows_cap >= fp8bs_moe_max_rows(tokens, topk, num_experts).
+ *   All pointers 4-byte aligned.  No output may overlap topk_ids.
+ */
+int fp8bs_moe_route(const int32_t* topk_ids, int64_t tokens, int64_t topk, int64_t num_experts,
+                    int32_t* seg_offsets, int32_t* slot_rows, int32_t* row_token, int64_t rows_cap,
+                    void* stream);
+
+/*
+ * Dispatch payload: each token row of x is coded once in 1x128 tiles and its
+ * codes and scales are stored to each of its slot rows, so row r of q equals
+ * row row_token[r] of fp8bs_quantize_act_1x128(x) bit for bit.  Padding rows
+ * (row_token == -1 within the last 128 rows of a segment) get +0 codes and
+ * scale 0; rows from seg_offsets[num_experts] to rows_cap are not written.
+ *   x            bf16 [tokens, hidden], row stride ldx elements
+ *   slot_rows    int32 [tokens, topk], seg_offsets int32 [num_experts + 1],
+ *   row_token    int32 [rows_cap]  (the outputs of fp8bs_moe_route)
+ *   q            E4M3 [rows_cap, hidden], row stride ldq bytes
+ *   scales       f32  [rows_cap, hidden/128], contiguous
+ *   hidden % 128 == 0, 1 <= topk <= 64, 1 <= num_experts <= 65536.
+ * A slot row outside [0, rows_cap) is treated as dropped; segment bounds are
+ * clipped to [0, rows_cap].  Alignment: x and q 16 bytes, ldx % 8 == 0,
+ * ldq % 16 == 0, the int32 and float pointers 4 bytes.
+ */
+int fp8bs_moe_permute_quantize(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t ldx,
+                               const int32_t* slot_rows, int64_t topk, const int32_t* seg_offsets,
+                               const int32_t* row_token, int64_t num_experts, uint8_t* q, int64_t ldq,
+                               float* scales, int64_t rows_cap, void* stream);
+
+/*
+ * Combine: out[t, :] = sum over slots j of gates[t, j] * y[slot_rows[t, j], :],
+ * accumulated in FP32 in slot order (acc = fma(g, y, acc) from +0), rounded
+ * once to bf16 (nearest, ties to even).  Dropped slots (row -1, or a row
+ * outside [0, rows_cap)) add nothing and their gates are not used.
+ *   y          bf16 [rows_cap, n], row stride ldy elements (expert outputs)
+ *   slot_rows  int32 [tokens, topk], gates f32 [tokens, topk]
+ *   out        bf16 [tokens, n], row stride ldo elements
+ *   n % 8 == 0, 1 <= topk <= 64, tokens >= 0 (0: nothing is written).
+ * Alignment: y and out 16 bytes, ldy % 8 == 0, ldo % 8 == 0, slot_rows and
+ * gates 4 bytes.  out must not overlap y.
+ */
+int fp8bs_moe_combine(const uint16_t* y, int64_t ldy, int64_t rows_cap, const int32_t* slot_rows,
+                      const float* gates, int64_t tokens, int64_t topk, int64_t n, uint16_t* out,
+                      int64_t ldo, void* stream);
 
 /* Short English text for a status code (static storage, never NULL). */
 const char* fp8bs_status_string(int status);

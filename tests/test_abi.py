@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_five_calls():
     names = declared_functions()
     for n in ("fp8bs_quantize_act_1x128", "fp8bs_quantize_w_128x128", "fp8bs_gemm", "fp8bs_grouped_gemm",
-              "fp8bs_gemm_wgrad", "fp8bs_status_string"):
+              "fp8bs_gemm_wgrad", "fp8bs_status_string", "fp8bs_moe_max_rows", "fp8bs_moe_route",
+              "fp8bs_moe_permute_quantize", "fp8bs_moe_combine"):
         assert n in names
 
 
@@ -124,3 +125,48 @@ def test_binding_has_the_c_names():
     for name in declared_functions():
         if name != "fp8bs_status_string":
             assert callable(getattr(lib, name)), name
+
+
+def test_moe_max_rows(raw):
+    f = raw.fp8bs_moe_max_rows
+    assert f(4096, 8, 256) == (32768 + 127 * 256) // 128 * 128
+    assert f(4, 2, 3) == 384 and f(2, 1, 1000) == 256 and f(0, 8, 256) == 0
+    assert f(-1, 8, 256) == ESHAPE and f(10, 0, 4) == ESHAPE and f(10, 65, 4) == ESHAPE
+    assert f(10, 8, 0) == ESHAPE and f(10, 8, 65537) == ESHAPE
+    assert f(1 << 28, 8, 256) == ESHAPE                             # rows past int32
+
+
+def test_moe_route_validation(raw):
+    f = raw.fp8bs_moe_route
+    cap = raw.fp8bs_moe_max_rows(100, 8, 256)
+    assert f(P, 100, 8, 256, P, P, None, cap, None) == ENULL
+    assert f(P, 100, 8, 256, P, P, P, cap - 128, None) == ESHAPE     # capacity below the bound
+    assert f(P, 100, 8, 1025, P, P, P, 1 << 20, None) == ESHAPE      # more experts than one workgroup sorts
+    assert f(P, 100, 0, 256, P, P, P, cap, None) == ESHAPE
+    assert f(P, -1, 8, 256, P, P, P, cap, None) == ESHAPE
+    assert f(P + 2, 100, 8, 256, P, P, P, cap, None) == EALIGN
+
+
+def test_moe_permute_quantize_validation(raw):
+    f = raw.fp8bs_moe_permute_quantize
+    assert f(P, 100, 7168, 7168, P, 8, P, P, 256, None, 7168, P, 4096, None) == ENULL
+    assert f(P, 100, 7100, 7168, P, 8, P, P, 256, P, 7168, P, 4096, None) == ESHAPE   # hidden % 128
+    assert f(P, 100, 7168, 7040, P, 8, P, P, 256, P, 7168, P, 4096, None) == ESHAPE   # ldx < hidden
+    assert f(P, 100, 7168, 7168, P, 8, P, P, 256, P, 7040, P, 4096, None) == ESHAPE   # ldq < hidden
+    assert f(P, 100, 7168, 7168, P, 65, P, P, 256, P, 7168, P, 4096, None) == ESHAPE  # topk
+    assert f(P, 100, 7168, 7168, P, 8, P, P, 256, P, 7168, P, -1, None) == ESHAPE     # capacity
+    assert f(P, 100, 7168, 7172, P, 8, P, P, 256, P, 7168, P, 4096, None) == EALIGN   # ldx % 8
+    assert f(P, 100, 7168, 7168, P, 8, P, P, 256, P, 7176, P, 4096, None) == EALIGN   # ldq % 16
+    assert f(P_ODD, 100, 7168, 7168, P, 8, P, P, 256, P, 7168, P, 4096, None) == EALIGN
+
+
+def test_moe_combine_validation(raw):
+    f = raw.fp8bs_moe_combine
+    assert f(P, 7168, 4096, P, None, 100, 8, 7168, P, 7168, None) == ENULL
+    assert f(P, 7168, 4096, P, P, 100, 8, 7164, P, 7168, None) == ESHAPE      # n % 8
+    assert f(P, 7160, 4096, P, P, 100, 8, 7168, P, 7168, None) == ESHAPE      # ldy < n
+    assert f(P, 7168, 4096, P, P, 100, 0, 7168, P, 7168, None) == ESHAPE      # topk
+    assert f(P, 7168, 4096, P, P, -1, 8, 7168, P, 7168, None) == ESHAPE
+    assert f(P, 7172, 4096, P, P, 100, 8, 7168, P, 7168, None) == EALIGN      # ldy % 8
+    assert f(P_ODD, 7168, 4096, P, P, 100, 8, 7168, P, 7168, None) == EALIGN
+    assert f(P, 7168, 4096, P, P, 0, 8, 7168, P, 7168, None) == OK            # no tokens: nothing to do
