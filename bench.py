@@ -39,6 +39,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "gemm": ["fp8_fine_grained_act_amd/csrc/gemm.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
     "quant": ["fp8_fine_grained_act_amd/csrc/quantize.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
+    "moe": ["fp8_fine_grained_act_amd/csrc/moe.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
 }
 
 
@@ -165,36 +166,72 @@ def build_layer_step(lib, cfg_name, rotate, dual=True):
 
 
 def build_grouped_step(lib, rotate):
+    """Calls of the MoE routed-expert forward around the grouped GEMM (config c4 shapes).
+
+    route (expert-major padded layout from the top-k ids) -> dispatch payload
+    (token rows coded once in 1x128 tiles, stored to their k rows) -> quantize
+    every expert's weight -> grouped GEMM over the row capacity -> combine
+    (gate-weighted sum of each token's k expert-output rows, bf16).  The
+    combine's expert outputs are [capacity, 7168] bf16 (the model width, the
+    shape the down projection returns); they are drawn once on the device.
+    No call reads a size back to the host.
+    """
     import numpy as np
     import torch
 
-    from workloads import config_by_name, device_expert_weights, grouped_inputs_host
+    from workloads import config_by_name, device_expert_weights, moe_dispatch_inputs, moe_routing
 
     cfg = config_by_name("c4")
-    g = grouped_inputs_host(cfg, with_weights=False)
-    off, counts = g["offsets"], g["counts"]
-    rows, k, n, num_e = int(off[-1]), cfg["K"], cfg["N"], cfg["experts"]
-    x = dev_bf16(g["x"])
+    d = moe_dispatch_inputs(cfg)
+    route = moe_routing(cfg)
+    counts, total = route["counts"], int(route["offsets"][-1])
+    tokens, topk = d["ids"].shape
+    k, n, num_e = cfg["K"], cfg["N"], cfg["experts"]
+    cap = lib.fp8bs_moe_max_rows(tokens, topk, num_e)
+    x = dev_bf16(d["x"])
+    ids = torch.from_numpy(d["ids"]).cuda()
+    gates = torch.from_numpy(d["gates"]).cuda()
     w = device_expert_weights(cfg)
-    seg = torch.from_numpy(off.astype(np.int32)).cuda()
-    qx, sx = torch.empty((rows, k), dtype=torch.uint8, device="cuda"), torch.empty(
-        (rows, k // 128), dtype=torch.float32, device="cuda")
-    qw, sw = torch.empty((num_e, n, k), dtype=torch.uint8, device="cuda"), torch.empty(
-        (num_e, n // 128, k // 128), dtype=torch.float32, device="cuda")
-    y = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4004)
+    y_down = torch.randn((cap, k), generator=gen, device="cuda").to(torch.bfloat16)
+    i32, u8, f32, bf16 = torch.int32, torch.uint8, torch.float32, torch.bfloat16
+    e = lambda *s, dt: torch.empty(s, dtype=dt, device="cuda")  # noqa: E731
+    seg, slot, tok = e(num_e + 1, dt=i32), e(tokens, topk, dt=i32), e(cap, dt=i32)
+    qx, sx = e(cap, k, dt=u8), e(cap, k // 128, dt=f32)
+    qw, sw = e(num_e, n, k, dt=u8), e(num_e, n // 128, k // 128, dt=f32)
+    y = e(cap, n, dt=bf16)
+    out = e(tokens, k, dt=bf16)
     state = {"i": 0}
-    real = float(counts.sum())
+    pairs = int(counts.sum())
+    seg_rows = np.diff(route["offsets"])
+    scanned = int(np.minimum(seg_rows, 128).sum())          # row tokens read by the padding workgroups
     calls = [
-        Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, q=qx, scales=sx),
-             nbytes=rows * k * 3 + rows * k // 128 * 4, outs=(qx, sx)),
+        Call("moe_route", "moe", lambda: lib.fp8bs_moe_route(ids, num_e, rows_cap=cap, seg_offsets=seg,
+                                                                slot_rows=slot, row_token=tok),
+             nbytes=tokens * topk * 4 * 2 + cap * 4 + (num_e + 1) * 4, outs=(seg, slot, tok)),
+        Call("moe_dispatch_x", "moe", lambda: lib.fp8bs_moe_permute_quantize(x, slot, seg, tok, q=qx, scales=sx),
+             nbytes=tokens * k * 2 + tokens * topk * 4 + scanned * 4 + total * (k + k // 128 * 4),
+             outs=(qx, sx)),
         Call("quant_w_experts", "quant", lambda: lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw),
              nbytes=num_e * n * k * 3 + num_e * (n // 128) * (k // 128) * 4, outs=(qw, sw)),
         Call("gemm_grouped", "gemm", lambda: lib.fp8bs_grouped_gemm(qx, sx, seg, qw, sw, c=y),
-             flops=2.0 * real * n * k, outs=(y,)),
+             flops=2.0 * pairs * n * k, outs=(y,)),
+        Call("moe_combine", "moe", lambda: lib.fp8bs_moe_combine(y_down, slot, gates, out=out),
+             nbytes=pairs * k * 2 + tokens * topk * 8 + tokens * k * 2, outs=(out,)),
     ]
+    # rows past the padded total are never written; the replay check compares
+    # only what the step defines
+    for c in calls:
+        if c.name == "moe_dispatch_x":
+            c.outs = [qx[:total], sx[:total]]
+        elif c.name == "gemm_grouped":
+            c.outs = [y[:total]]
     desc = dict(workload="c4: MoE routed-expert forward, 4096 tokens x top-8 of 256 experts (Zipf 1.1), "
-                         "fused gate+up N=4096, K=7168; quantize X and all expert weights, grouped GEMM",
-                routed_rows=int(real), padded_rows=rows, experts=num_e, N=n, K=k,
+                         "fused gate+up N=4096, K=7168: route, dispatch (permute + 1x128 quantize), quantize all "
+                         "expert weights, grouped GEMM over the row capacity, combine of [capacity, 7168] bf16 "
+                         "expert outputs",
+                routed_rows=pairs, padded_rows=total, row_capacity=cap, experts=num_e, N=n, K=k,
                 gemm_flops_counted="real routed rows only")
     return calls, state, desc, None
 
@@ -451,6 +488,9 @@ def main():
         else:
             gb = c.nbytes / (avg * 1e-3) / 1e9
             ent.update(gbps=round(gb, 1), frac_hbm_peak=round(gb / HBM_PEAK_GBPS, 4))
+        tr = load_traffic(f"{args.config}:{c.name}", c.kind)
+        if tr is not None:
+            ent["traffic"] = tr
         kernels[c.name] = ent
     dom = max(calls, key=lambda c: sum(c.times_ms))
     avg = sum(dom.times_ms) / len(dom.times_ms) * 1e-3

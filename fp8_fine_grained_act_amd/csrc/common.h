@@ -138,6 +138,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// ---- streaming (non-temporal) 16-byte loads and stores ----------------------
+// For data touched once per kernel (a dispatch payload written far larger than
+// the caches, expert rows gathered once): the accesses carry the non-temporal
+// hint, so they do not displace other lines in the caches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_nt(void* p, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 // ---- buffer copies straight into LDS, and vmcnt waits ---------------------
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access, gfx9 family
 

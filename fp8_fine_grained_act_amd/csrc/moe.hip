@@ -11,7 +11,8 @@
 //
 //   moe_route_kernel     one workgroup: a stable counting sort of the
 //                        (token, slot) pairs by expert id, giving the padded
-//                        segment starts, each pair's row and each row's token
+//                        segment starts and each pair's row; with
+//   moe_route_rows_kernel  each row's token
 //   moe_dispatch_kernel  each token row is read once, coded once in 1x128
 //                        tiles and its codes and scales stored to its k rows;
 //                        one workgroup per expert zeroes its padding rows
@@ -38,18 +39,29 @@ constexpr int kMaxTopk = 64;               // a token's slots fit in one wave's 
 // Routing: wave w owns the pairs [lo_w, hi_w) (pairs in row-major
 // (token, slot) order, chunks in wave order), so "earlier pair" means an
 // earlier wave, or an earlier 64-pair step of the same wave, or a lower lane.
-//   1. per-wave histograms in LDS (atomic adds: counts do not depend on order)
-//   2. per expert: exclusive prefix over the waves, count, padded size; an
-//      exclusive scan of the padded sizes over the experts gives the segment
-//      starts; each wave's running row for expert e = start + its prefix
-//   3. each wave walks its chunk 64 pairs at a time: lanes holding the same
-//      expert are found with one ballot per id bit, a pair's rank among them is
-//      the population count of the matching lower lanes, and the lowest such
-//      lane advances the running row by the group's size
-//   4. rows of padding (and rows past the padded total) get token -1
+//   1. each wave walks its chunk 64 pairs at a time: lanes holding the same
+//      expert are found with one ballot per id bit; a pair's rank among them
+//      is the population count of the matching lower lanes; its rank within
+//      the wave's chunk (the wave's running count for that expert, kept in
+//      LDS, plus that rank) goes to slot_rows for now, and the lowest lane of
+//      the group advances the running count by the group's size
+//   2. per expert: exclusive prefix of the running counts over the waves,
+//      count, padded size; an exclusive scan of the padded sizes over the
+//      experts gives the segment starts; each wave's first row for expert e is
+//      start + its prefix
+//   3. every pair adds its wave's first row for its expert to its rank
+//      (independent pairs: no chain)
+//   4. padding rows and the rows past the padded total get token -1, written
+//      by whole waves in runs
+// The ids of 16 steps are loaded together, so each wave waits for memory once
+// per 1024 pairs.  The row -> token entries of the routed pairs are scattered
+// by moe_route_rows_kernel, a separate grid over the pairs: from one
+// workgroup those 4-byte stores to 64 different rows per instruction would
+// serialize in the workgroup's one memory pipeline.
+constexpr int kRouteBatch = 16;
+
 __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restrict__ ids, int64_t pairs,
-                                                         int topk, int num_e, int id_bits,
-                                                         int32_t* __restrict__ seg,
+                                                         int num_e, int id_bits, int32_t* __restrict__ seg,
                                                          int32_t* __restrict__ slot_rows,
                                                          int32_t* __restrict__ row_token, int64_t cap) {
   __shared__ int next_row[kRouteWaves][kRouteMaxExperts];
@@ -64,9 +76,38 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restri
 
   const int64_t chunk = ((pairs + kRouteWaves - 1) / kRouteWaves + 63) / 64 * 64;
   const int64_t lo = min(pairs, (int64_t)w * chunk), hi = min(pairs, lo + chunk);
-  for (int64_t i = lo + lane; i < hi; i += 64) {
-    const int e = ids[i];
-    if (e >= 0 && e < num_e) atomicAdd(&next_row[w][e], 1);
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t b0 = lo; b0 < hi; b0 += 64 * kRouteBatch) {
+    int ev[kRouteBatch];
+#pragma unroll
+    for (int st = 0; st < kRouteBatch; ++st) {
+      const int64_t i = b0 + 64 * st + lane;
+      ev[st] = i < hi ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int st = 0; st < kRouteBatch; ++st) {
+      if (b0 + 64 * st >= hi) break;
+      const int64_t i = b0 + 64 * st + lane;
+      const int e = ev[st];
+      const bool ok = i < hi && e >= 0 && e < num_e;
+      uint64_t same = __ballot(ok);
+#pragma unroll
+      for (int b = 0; b < 10; ++b) {
+        if (b < id_bits) {
+          const bool bit = (e >> b) & 1;
+          const uint64_t on = __ballot(ok && bit);
+          same &= bit ? on : ~on;
+        }
+      }
+      if (ok) {
+        const int rank = __popcll(same & below);
+        const int base = next_row[w][e];
+        slot_rows[i] = base + rank;
+        if (rank == 0) next_row[w][e] = base + __popcll(same);
+      } else if (i < hi) {
+        slot_rows[i] = -1;
+      }
+    }
   }
   __syncthreads();
 
@@ -101,44 +142,51 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restri
   }
   __syncthreads();
 
-  const uint64_t below = (1ull << lane) - 1ull;
-  for (int64_t i0 = lo; i0 < hi; i0 += 64) {
-    const int64_t i = i0 + lane;
-    const bool in = i < hi;
-    const int e = in ? ids[i] : -1;
-    const bool ok = in && e >= 0 && e < num_e;
-    uint64_t same = __ballot(ok);
-    for (int b = 0; b < id_bits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t on = __ballot(ok && bit);
-      same &= bit ? on : ~on;
+  for (int64_t b0 = lo; b0 < hi; b0 += 64 * kRouteBatch) {
+    int ev[kRouteBatch], rv[kRouteBatch];
+#pragma unroll
+    for (int st = 0; st < kRouteBatch; ++st) {
+      const int64_t i = b0 + 64 * st + lane;
+      ev[st] = i < hi ? ids[i] : -1;
+      rv[st] = i < hi ? slot_rows[i] : -1;            // this lane's own store of step 1
     }
-    if (ok) {
-      const int rank = __popcll(same & below);
-      const int row = next_row[w][e] + rank;
-      slot_rows[i] = row;
-      row_token[row] = (int)(i / topk);
-      if (rank == 0) next_row[w][e] = row + __popcll(same);
-    } else if (in) {
-      slot_rows[i] = -1;
+#pragma unroll
+    for (int st = 0; st < kRouteBatch; ++st) {
+      const int64_t i = b0 + 64 * st + lane;
+      if (i < hi && ev[st] >= 0 && ev[st] < num_e) slot_rows[i] = next_row[w][ev[st]] + rv[st];
     }
   }
 
-  if (tid < num_e)
-    for (int r = seg_s[tid] + cnt_s[tid]; r < seg_s[tid + 1]; ++r) row_token[r] = -1;
+  for (int e = w; e < num_e; e += kRouteWaves)
+    for (int r = seg_s[e] + cnt_s[e] + lane; r < seg_s[e + 1]; r += 64) row_token[r] = -1;
   for (int64_t r = (int64_t)seg_s[num_e] + tid; r < cap; r += 1024) row_token[r] = -1;
 }
 
+// row -> token for every routed pair (the other rows were set by moe_route_kernel)
+__global__ __launch_bounds__(256) void moe_route_rows_kernel(const int32_t* __restrict__ slot_rows, int64_t pairs,
+                                                             int topk, int32_t* __restrict__ row_token,
+                                                             int64_t cap) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= pairs) return;
+  const int r = slot_rows[i];
+  if (r >= 0 && r < cap) row_token[r] = (int)(i / topk);
+}
+
 // ---------------------------------------------------------------------------
-// Dispatch payload.  Token blocks: 4 waves, one token per wave; 8 lanes per
+// Dispatch payload.  Token blocks: 4 waves, TPW tokens per wave; 8 lanes per
 // 128-element tile (16 bf16 each, two 16-byte loads), so one wave step covers
 // 8 tiles (2 KB of the row) and stores 8 x 1 KB of codes, one full 1 KB run
 // per destination row and store instruction.  The tile's amax, scale and codes
 // are computed exactly as by the 1x128 activation quantizer (a tile depends
 // only on its own 128 values), once per token, whatever k is.
-// Padding blocks (blockIdx.x >= token_blocks): expert e's padding rows lie in
-// the last 128 rows of its segment; each such row whose token is -1 gets +0
-// codes and scale 0.
+// Padding blocks come first in the grid (blockIdx.x < pad_blocks), so their
+// zero rows are written alongside the token blocks rather than after them:
+// with a skewed routing padding is a large share of the rows (21120 of 53888
+// for 4096 tokens, top-8 of 256 experts, Zipf 1.1).  Each padding row (token
+// -1) gets +0 codes and scale 0.  The routed rows' codes are stored with the
+// non-temporal hint (measured at that size: 98 -> 72 us; the hint on the
+// padding rows' zeros made it slower, and so did placing the padding blocks
+// after the token blocks or giving a wave more than one token).
 __device__ __forceinline__ uint32_t tile16_amax(const uint32_t in[8]) {
   constexpr uint32_t kMag = 0x7FFF7FFFu;
   const uint32_t m2 = max_u16x2(max_u16x2(max_u16x2(in[0] & kMag, in[1] & kMag), max_u16x2(in[2] & kMag, in[3] & kMag)),
@@ -146,121 +194,166 @@ __device__ __forceinline__ uint32_t tile16_amax(const uint32_t in[8]) {
   return max8_u32(max(m2 & 0xFFFFu, m2 >> 16));
 }
 
+constexpr int kPadParts = 4;                        // padding workgroups per expert
+
+template <int TPW>
 __global__ __launch_bounds__(256) void moe_dispatch_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t tokens, int hidden,
     const int32_t* __restrict__ slot_rows, int topk, const int32_t* __restrict__ seg,
     const int32_t* __restrict__ row_token, uint8_t* __restrict__ q, int64_t ldq,
-    float* __restrict__ scales, int64_t cap, int64_t token_blocks) {
+    float* __restrict__ scales, int64_t cap, int64_t pad_blocks) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int groups = hidden / kGroup;
-  if ((int64_t)blockIdx.x < token_blocks) {
-    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
-    if (t >= tokens) return;
-    int my_row = -1;                                   // lane j < topk: the row of slot j
-    if (lane < topk) {
-      const int r = slot_rows[t * topk + lane];
-      my_row = (r >= 0 && r < cap) ? r : -1;
-    }
-    const int sg = lane & 7;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + t * ldx + 16 * sg);   // 16 uint4 per tile
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    uint4 a = zero, b = zero;
-    if ((lane >> 3) < groups) {
-      a = xr[16 * (lane >> 3)];
-      b = xr[16 * (lane >> 3) + 1];
-    }
-    for (int g0 = 0; g0 < groups; g0 += 8) {
-      const int g = g0 + (lane >> 3);
-      uint4 na = zero, nb = zero;                      // next step's loads first
-      if (g + 8 < groups) {
-        na = xr[16 * (g + 8)];
-        nb = xr[16 * (g + 8) + 1];
-      }
-      const uint32_t in[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      const GroupScale gs = group_scale(tile16_amax(in));
-      uint4 o;
-      quant_run<8>(in, reinterpret_cast<uint32_t*>(&o), gs);
-      for (int j = 0; j < topk; ++j) {                // uniform loop: readlane sees every lane
-        const int row = __builtin_amdgcn_readlane(my_row, j);
-        if (row < 0 || g >= groups) continue;
-        *reinterpret_cast<uint4*>(q + (int64_t)row * ldq + (int64_t)g * kGroup + 16 * sg) = o;
-        if (sg == 0) scales[(int64_t)row * groups + g] = gs.s;
-      }
-      a = na;
-      b = nb;
-    }
-  } else {
-    const int64_t e = (int64_t)blockIdx.x - token_blocks;
+  if ((int64_t)blockIdx.x < pad_blocks) {
+    // padding: expert e's padding rows lie in the last 128 rows of its
+    // segment; workgroup (e, part) checks 32 of them, one wave per row
+    const int64_t e = (int64_t)blockIdx.x / kPadParts, part = (int64_t)blockIdx.x % kPadParts;
     int64_t hi = seg[e + 1];
     if (hi > cap) hi = cap;
     int64_t lo = seg[e];
-    if (lo < hi - kGroup) lo = hi - kGroup;
     if (lo < 0) lo = 0;
+    const int64_t r0 = hi - kGroup + part * (kGroup / kPadParts);
     const uint4 zero = make_uint4(0, 0, 0, 0);
-    for (int64_t r = lo + wave; r < hi; r += 4) {
-      if (row_token[r] >= 0) continue;
+    for (int64_t r = r0 + wave; r < r0 + kGroup / kPadParts; r += 4) {
+      if (r < lo || r >= hi || row_token[r] >= 0) continue;
       uint8_t* qr = q + r * ldq;
       for (int c = 16 * lane; c < hidden; c += 1024) *reinterpret_cast<uint4*>(qr + c) = zero;
       for (int c = lane; c < groups; c += 64) scales[r * groups + c] = 0.0f;
+    }
+  } else {
+    // TPW tokens per wave, their steps interleaved (more loads in flight)
+    const int64_t t0 = (((int64_t)blockIdx.x - pad_blocks) * 4 + wave) * TPW;
+    if (t0 >= tokens) return;
+    const int sg = lane & 7;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    int my_row[TPW];                                   // lane j < topk: the row of slot j
+    const uint4* xr[TPW];                              // 16 uint4 per tile
+    uint4 a[TPW], b[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const bool live = t0 + u < tokens;
+      const int64_t t = live ? t0 + u : t0;
+      my_row[u] = -1;
+      if (live && lane < topk) {
+        const int r = slot_rows[t * topk + lane];
+        my_row[u] = (r >= 0 && r < cap) ? r : -1;
+      }
+      xr[u] = reinterpret_cast<const uint4*>(x + t * ldx + 16 * sg);
+      a[u] = zero;
+      b[u] = zero;
+      if ((lane >> 3) < groups) {
+        a[u] = xr[u][16 * (lane >> 3)];
+        b[u] = xr[u][16 * (lane >> 3) + 1];
+      }
+    }
+    for (int g0 = 0; g0 < groups; g0 += 8) {
+      const int g = g0 + (lane >> 3);
+      uint4 na[TPW], nb[TPW];                          // next step's loads first
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        na[u] = zero;
+        nb[u] = zero;
+        if (g + 8 < groups) {
+          na[u] = xr[u][16 * (g + 8)];
+          nb[u] = xr[u][16 * (g + 8) + 1];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const uint32_t in[8] = {a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w};
+        const GroupScale gs = group_scale(tile16_amax(in));
+        uint4 o;
+        quant_run<8>(in, reinterpret_cast<uint32_t*>(&o), gs);
+        for (int j = 0; j < topk; ++j) {              // uniform loop: readlane sees every lane
+          const int row = __builtin_amdgcn_readlane(my_row[u], j);
+          if (row < 0 || g >= groups) continue;
+          store_nt(q + (int64_t)row * ldq + (int64_t)g * kGroup + 16 * sg, o);
+          if (sg == 0) scales[(int64_t)row * groups + g] = gs.s;
+        }
+        a[u] = na[u];
+        b[u] = nb[u];
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one wave per token, 8 bf16 columns per lane and step (512 columns
-// per wave step).  The k rows' 16-byte pieces are loaded together, 8 slots
-// at a time, then folded in slot order: acc = fma(g_j, y_j, acc) in FP32,
-// starting from +0; a dropped slot (row -1 or outside the capacity) is
+// Combine: TPW tokens per wave, 8 bf16 columns per lane and step (512 columns
+// per wave step).  A token's k rows' 16-byte pieces are loaded together, 8
+// slots at a time, then folded in slot order: acc = fma(g_j, y_j, acc) in
+// FP32, starting from +0; a dropped slot (row -1 or outside the capacity) is
 // skipped.  The sum is rounded once to bf16 (nearest, ties to even).
+// The expert rows are read once, with the non-temporal hint (measured on
+// 4096 tokens x top-8, 7168 columns: 110 -> 98.5 us; the hint on the output
+// store, or more tokens per wave, did not help).
+template <int TPW>
 __global__ __launch_bounds__(256) void moe_combine_kernel(
     const uint16_t* __restrict__ y, int64_t ldy, int64_t cap, const int32_t* __restrict__ slot_rows,
     const float* __restrict__ gates, int64_t tokens, int topk, int n, uint16_t* __restrict__ out,
     int64_t ldo) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  if (t >= tokens) return;
-  int my_row = -1;
-  float my_g = 0.0f;
-  if (lane < topk) {
-    const int r = slot_rows[t * topk + lane];
-    my_row = (r >= 0 && r < cap) ? r : -1;
-    my_g = gates[t * topk + lane];
+  const int64_t t0 = ((int64_t)blockIdx.x * 4 + wave) * TPW;
+  if (t0 >= tokens) return;
+  int my_row[TPW];
+  float my_g[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    my_row[u] = -1;
+    my_g[u] = 0.0f;
+    if (t0 + u < tokens && lane < topk) {
+      const int r = slot_rows[(t0 + u) * topk + lane];
+      my_row[u] = (r >= 0 && r < cap) ? r : -1;
+      my_g[u] = gates[(t0 + u) * topk + lane];
+    }
   }
   for (int c0 = 0; c0 < n; c0 += 512) {              // uniform loop: readlane sees every lane
     const int c = c0 + 8 * lane;
     const bool live = c < n;
-    float acc[8];
+    float acc[TPW][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
     for (int j0 = 0; j0 < topk; j0 += 8) {
-      uint4 v[8];
-      int rows[8];
+      uint4 v[TPW][8];
+      int rows[TPW][8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        rows[jj] = j0 + jj < topk ? __builtin_amdgcn_readlane(my_row, j0 + jj) : -1;
-        v[jj] = rows[jj] >= 0 && live ? *reinterpret_cast<const uint4*>(y + (int64_t)rows[jj] * ldy + c)
-                                      : make_uint4(0, 0, 0, 0);
-      }
+      for (int u = 0; u < TPW; ++u)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        if (rows[jj] < 0) continue;
-        const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), j0 + jj));
-        const uint32_t d[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = __builtin_fmaf(g, bf16_lo(d[i]), acc[2 * i]);
-          acc[2 * i + 1] = __builtin_fmaf(g, bf16_hi(d[i]), acc[2 * i + 1]);
+        for (int jj = 0; jj < 8; ++jj) {
+          rows[u][jj] = j0 + jj < topk ? __builtin_amdgcn_readlane(my_row[u], j0 + jj) : -1;
+          v[u][jj] = rows[u][jj] >= 0 && live
+                         ? load_nt(y + (int64_t)rows[u][jj] * ldy + c)
+                         : make_uint4(0, 0, 0, 0);
         }
-      }
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          if (rows[u][jj] < 0) continue;
+          const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g[u]), j0 + jj));
+          const uint32_t d[4] = {v[u][jj].x, v[u][jj].y, v[u][jj].z, v[u][jj].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[u][2 * i] = __builtin_fmaf(g, bf16_lo(d[i]), acc[u][2 * i]);
+            acc[u][2 * i + 1] = __builtin_fmaf(g, bf16_hi(d[i]), acc[u][2 * i + 1]);
+          }
+        }
     }
-    uint4 o;
-    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-    o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-    o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-    if (live) *reinterpret_cast<uint4*>(out + t * ldo + c) = o;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      uint4 o;
+      o.x = f32_to_bf16_rne(acc[u][0]) | (f32_to_bf16_rne(acc[u][1]) << 16);
+      o.y = f32_to_bf16_rne(acc[u][2]) | (f32_to_bf16_rne(acc[u][3]) << 16);
+      o.z = f32_to_bf16_rne(acc[u][4]) | (f32_to_bf16_rne(acc[u][5]) << 16);
+      o.w = f32_to_bf16_rne(acc[u][6]) | (f32_to_bf16_rne(acc[u][7]) << 16);
+      if (live && t0 + u < tokens) *reinterpret_cast<uint4*>(out + (t0 + u) * ldo + c) = o;
+    }
   }
 }
+
+constexpr int kDispatchTPW = 1;
+constexpr int kCombineTPW = 1;
 
 static int64_t max_rows(int64_t tokens, int64_t topk, int64_t num_e) {
   const int64_t pairs = tokens * topk;
@@ -293,9 +386,12 @@ extern "C" int fp8bs_moe_route(const int32_t* topk_ids, int64_t tokens, int64_t 
     return FP8BS_ERR_ALIGN;
   int bits = 0;
   while ((1LL << bits) < num_experts) ++bits;
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(64 * kRouteWaves), 0, (hipStream_t)stream, topk_ids,
-                     tokens * topk, (int)topk, (int)num_experts, bits, seg_offsets, slot_rows, row_token,
-                     rows_cap);
+  const int64_t pairs = tokens * topk;
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(64 * kRouteWaves), 0, (hipStream_t)stream, topk_ids, pairs,
+                     (int)num_experts, bits, seg_offsets, slot_rows, row_token, rows_cap);
+  if (pairs > 0)
+    hipLaunchKernelGGL(moe_route_rows_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, slot_rows, pairs, (int)topk, row_token, rows_cap);
   return launch_status();
 }
 
@@ -311,12 +407,13 @@ extern "C" int fp8bs_moe_permute_quantize(const uint16_t* x, int64_t tokens, int
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4) || !aligned(slot_rows, 4) ||
       !aligned(seg_offsets, 4) || !aligned(row_token, 4) || ldx % 8 || ldq % 16)
     return FP8BS_ERR_ALIGN;
-  const int64_t token_blocks = (tokens + 3) / 4;
-  const int64_t grid = token_blocks + num_experts;
+  const int64_t token_blocks = (tokens + 4 * kDispatchTPW - 1) / (4 * kDispatchTPW);
+  const int64_t pad_blocks = num_experts * kPadParts;
+  const int64_t grid = pad_blocks + token_blocks;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL(moe_dispatch_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, x, ldx,
+  hipLaunchKernelGGL(moe_dispatch_kernel<kDispatchTPW>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, x, ldx,
                      tokens, (int)hidden, slot_rows, (int)topk, seg_offsets, row_token, q, ldq, scales, rows_cap,
-                     token_blocks);
+                     pad_blocks);
   return launch_status();
 }
 
@@ -331,9 +428,9 @@ extern "C" int fp8bs_moe_combine(const uint16_t* y, int64_t ldy, int64_t rows_ca
       ldo % 8)
     return FP8BS_ERR_ALIGN;
   if (tokens == 0) return FP8BS_OK;
-  const int64_t grid = (tokens + 3) / 4;
+  const int64_t grid = (tokens + 4 * kCombineTPW - 1) / (4 * kCombineTPW);
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, y, ldy,
+  hipLaunchKernelGGL(moe_combine_kernel<kCombineTPW>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, y, ldy,
                      rows_cap, slot_rows, gates, tokens, (int)topk, (int)n, out, ldo);
   return launch_status();
 }
