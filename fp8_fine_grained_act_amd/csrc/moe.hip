@@ -32,19 +32,24 @@
 namespace fp8bs {
 
 constexpr int kRouteWaves = 16;            // one 1024-thread workgroup
-constexpr int kRouteMaxExperts = 1024;
+constexpr int kRouteMaxExperts = 512;       // LDS: 96 KB of per-wave tables
 constexpr int kMaxTopk = 64;               // a token's slots fit in one wave's lanes
 
 // ---------------------------------------------------------------------------
 // Routing: wave w owns the pairs [lo_w, hi_w) (pairs in row-major
 // (token, slot) order, chunks in wave order), so "earlier pair" means an
 // earlier wave, or an earlier 64-pair step of the same wave, or a lower lane.
-//   1. each wave walks its chunk 64 pairs at a time: lanes holding the same
-//      expert are found with one ballot per id bit; a pair's rank among them
-//      is the population count of the matching lower lanes; its rank within
-//      the wave's chunk (the wave's running count for that expert, kept in
-//      LDS, plus that rank) goes to slot_rows for now, and the lowest lane of
-//      the group advances the running count by the group's size
+//   1. each wave walks its chunk 64 pairs at a time: every lane ORs its lane
+//      bit into its expert's 64-bit mask in LDS (an atomic OR: the order of
+//      the lanes does not matter), then reads the mask back: the lanes of the
+//      step that hold the same expert.  A pair's rank among them is the
+//      population count of the lower lanes; its rank within the wave's chunk
+//      (the wave's running count for that expert, also in LDS, plus that
+//      rank) goes to slot_rows for now, and the lowest lane of the group
+//      advances the running count by the group's size and clears the mask.
+//      (One ballot per id bit instead: 38 us against 26 us for the whole
+//      routing of 32768 pairs over 256 experts, the ballots' vector work
+//      saturating the workgroup's one compute unit.)
 //   2. per expert: exclusive prefix of the running counts over the waves,
 //      count, padded size; an exclusive scan of the padded sizes over the
 //      experts gives the segment starts; each wave's first row for expert e is
@@ -61,17 +66,21 @@ constexpr int kMaxTopk = 64;               // a token's slots fit in one wave's 
 constexpr int kRouteBatch = 16;
 
 __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restrict__ ids, int64_t pairs,
-                                                         int num_e, int id_bits, int32_t* __restrict__ seg,
+                                                         int num_e, int32_t* __restrict__ seg,
                                                          int32_t* __restrict__ slot_rows,
                                                          int32_t* __restrict__ row_token, int64_t cap) {
   __shared__ int next_row[kRouteWaves][kRouteMaxExperts];
   __shared__ int seg_s[kRouteMaxExperts + 1];
   __shared__ int cnt_s[kRouteMaxExperts];
   __shared__ int wave_sum[kRouteWaves];
+  __shared__ unsigned long long match[kRouteWaves][kRouteMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   if (tid < num_e)
-    for (int v = 0; v < kRouteWaves; ++v) next_row[v][tid] = 0;
+    for (int v = 0; v < kRouteWaves; ++v) {
+      next_row[v][tid] = 0;
+      match[v][tid] = 0;
+    }
   __syncthreads();
 
   const int64_t chunk = ((pairs + kRouteWaves - 1) / kRouteWaves + 63) / 64 * 64;
@@ -90,20 +99,16 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restri
       const int64_t i = b0 + 64 * st + lane;
       const int e = ev[st];
       const bool ok = i < hi && e >= 0 && e < num_e;
-      uint64_t same = __ballot(ok);
-#pragma unroll
-      for (int b = 0; b < 10; ++b) {
-        if (b < id_bits) {
-          const bool bit = (e >> b) & 1;
-          const uint64_t on = __ballot(ok && bit);
-          same &= bit ? on : ~on;
-        }
-      }
+      if (ok) atomicOr(&match[w][e], 1ull << lane);
       if (ok) {
+        const uint64_t same = match[w][e];
         const int rank = __popcll(same & below);
         const int base = next_row[w][e];
         slot_rows[i] = base + rank;
-        if (rank == 0) next_row[w][e] = base + __popcll(same);
+        if (rank == 0) {
+          next_row[w][e] = base + __popcll(same);
+          match[w][e] = 0;
+        }
       } else if (i < hi) {
         slot_rows[i] = -1;
       }
@@ -384,11 +389,9 @@ extern "C" int fp8bs_moe_route(const int32_t* topk_ids, int64_t tokens, int64_t 
   if (rows_cap < max_rows(tokens, topk, num_experts) || rows_cap > 0x7FFFFFFFLL) return FP8BS_ERR_SHAPE;
   if (!aligned(topk_ids, 4) || !aligned(seg_offsets, 4) || !aligned(slot_rows, 4) || !aligned(row_token, 4))
     return FP8BS_ERR_ALIGN;
-  int bits = 0;
-  while ((1LL << bits) < num_experts) ++bits;
   const int64_t pairs = tokens * topk;
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(64 * kRouteWaves), 0, (hipStream_t)stream, topk_ids, pairs,
-                     (int)num_experts, bits, seg_offsets, slot_rows, row_token, rows_cap);
+                     (int)num_experts, seg_offsets, slot_rows, row_token, rows_cap);
   if (pairs > 0)
     hipLaunchKernelGGL(moe_route_rows_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
                        (hipStream_t)stream, slot_rows, pairs, (int)topk, row_token, rows_cap);

@@ -206,7 +206,7 @@ int64_t fp8bs_moe_max_rows(int64_t tokens, int64_t topk, int64_t num_experts);
  *   slot_rows    int32 [tokens, topk]  out: row of each pair (-1: dropped id)
  *   row_token    int32 [rows_cap]      out: token of each row; -1 for padding
  *                rows and for every row from the padded total to rows_cap
- *   1 <= num_experts <= 1024, 1 <= topk <= 64, tokens >= 0 (0: all segments
+ *   1 <= num_experts <= 512, 1 <= topk <= 64, tokens >= 0 (0: all segments
  *   empty), rows_cap >= fp8bs_moe_max_rows(tokens, topk, num_experts).
  *   All pointers 4-byte aligned.  No output may overlap topk_ids.
  */

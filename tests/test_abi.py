@@ -141,7 +141,7 @@ def test_moe_route_validation(raw):
     cap = raw.fp8bs_moe_max_rows(100, 8, 256)
     assert f(P, 100, 8, 256, P, P, None, cap, None) == ENULL
     assert f(P, 100, 8, 256, P, P, P, cap - 128, None) == ESHAPE     # capacity below the bound
-    assert f(P, 100, 8, 1025, P, P, P, 1 << 20, None) == ESHAPE      # more experts than one workgroup sorts
+    assert f(P, 100, 8, 513, P, P, P, 1 << 20, None) == ESHAPE       # more experts than one workgroup sorts
     assert f(P, 100, 0, 256, P, P, P, cap, None) == ESHAPE
     assert f(P, -1, 8, 256, P, P, P, cap, None) == ESHAPE
     assert f(P + 2, 100, 8, 256, P, P, P, cap, None) == EALIGN

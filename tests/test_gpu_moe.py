@@ -42,7 +42,7 @@ def _check_route(lib, ids, num_e, label):
     return r
 
 
-@pytest.mark.parametrize("t,k,e,seed", [(1, 1, 1, 0), (37, 3, 5, 1), (300, 8, 256, 2), (2000, 2, 1024, 3),
+@pytest.mark.parametrize("t,k,e,seed", [(1, 1, 1, 0), (37, 3, 5, 1), (300, 8, 256, 2), (2000, 2, 512, 3),
                                         (5, 64, 7, 4), (129, 1, 1, 5)])
 def test_route_random_ids_with_dropped_pairs(gpu_lib, t, k, e, seed):
     rng = np.random.default_rng(seed)
