@@ -80,3 +80,63 @@ def test_layer_pass_graph_replays_match_eager(gpu_lib):
             assert torch.equal(_bits(t), r), f"replay {rep}: output {i} differs from the eager pass"
     print(f"[graph] {len(outs)} outputs bit-identical to eager on 4 replays", flush=True)
     assert np.isfinite(bf16_values_host(y)).all()
+
+
+def test_moe_forward_graph_replays_match_eager(gpu_lib):
+    """Route -> dispatch -> grouped GEMM over the row capacity -> combine, captured once.
+
+    No call reads a size back to the host, so the whole MoE forward is one graph.
+    The eager layout is checked against the oracle; replays with poisoned outputs
+    and unrelated eager work in between must reproduce the eager bits (rows past
+    the padded total are not defined outputs and are left out)."""
+    from oracle.moe import moe_route
+    from workloads import moe_dispatch_inputs, normal_bf16
+
+    cfg = dict(tokens=300, topk=8, experts=16, zipf_s=1.1, seed=31, K=256)
+    d = moe_dispatch_inputs(cfg)
+    n = 256
+    w = to_dev_bf16(normal_bf16(np.random.default_rng(32), (16, n, 256), 0.02))
+    ids, gates, x = (torch.from_numpy(d["ids"]).cuda(), torch.from_numpy(d["gates"]).cuda(),
+                     to_dev_bf16(d["x"]))
+    cap = gpu_lib.fp8bs_moe_max_rows(300, 8, 16)
+    i32, u8, f32, bf16 = torch.int32, torch.uint8, torch.float32, torch.bfloat16
+    e = lambda *s, dt: torch.empty(s, dtype=dt, device="cuda")  # noqa: E731
+    seg, slot, tok = e(17, dt=i32), e(300, 8, dt=i32), e(cap, dt=i32)
+    q, s = e(cap, 256, dt=u8), e(cap, 2, dt=f32)
+    qw, sw = e(16, n, 256, dt=u8), e(16, n // 128, 2, dt=f32)
+    y, out = e(cap, n, dt=bf16), e(300, n, dt=bf16)
+
+    def moe_pass():
+        gpu_lib.fp8bs_moe_route(ids, 16, rows_cap=cap, seg_offsets=seg, slot_rows=slot, row_token=tok)
+        gpu_lib.fp8bs_moe_permute_quantize(x, slot, seg, tok, q=q, scales=s)
+        gpu_lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw)
+        gpu_lib.fp8bs_grouped_gemm(q, s, seg, qw, sw, c=y)
+        gpu_lib.fp8bs_moe_combine(y, slot, gates, out=out)
+
+    moe_pass()
+    torch.cuda.synchronize()
+    r = moe_route(d["ids"], 16)
+    total = int(r["seg_offsets"][-1])
+    assert np.array_equal(seg.cpu().numpy(), r["seg_offsets"]) and np.array_equal(tok.cpu().numpy(), r["row_token"])
+    outs = [seg, slot, tok, q[:total], s[:total], qw, sw, y[:total], out]
+    ref = [_bits(t).clone() for t in outs]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            moe_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    other = to_dev_bf16(gemm_inputs("c1", seed=78)["a"])
+    for rep in range(4):
+        for t in (seg, slot, tok, q, s, qw, sw, y, out):
+            t.view(torch.uint8).fill_(0x5A)
+        gpu_lib.fp8bs_quantize_act_1x128(other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, rb) in enumerate(zip(outs, ref)):
+            assert torch.equal(_bits(t), rb), f"replay {rep}: MoE output {i} differs from the eager pass"
