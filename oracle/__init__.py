@@ -30,7 +30,8 @@ Modules
 -------
 e4m3      exact decode table and RNE/saturating encoder for OCP E4M3
 bf16      bfloat16 <-> float conversions (exact decode, RNE encode)
-quantize  1x128 activation tiles, 128x128 weight blocks, transposed tiles
+quantize  1x128 activation tiles, 128x128 weight blocks, transposed tiles,
+          re-tiling of a cached (FP8) activation along its rows
 gemm      block-scaled GEMMs: forward (NT), activation gradient (NN),
           weight gradient (per-row scales on both operands), MoE grouped
 moe       MoE dispatch layout (expert-major, 128-padded segments), dispatch
@@ -43,14 +44,16 @@ brute force, textbook special cases).  No function here is "parity unpinned".
 
 from .e4m3 import E4M3_MAX, e4m3_decode_table, e4m3_decode, e4m3_encode
 from .bf16 import bf16_to_f32, f32_to_bf16_rne, f64_to_bf16_rne
-from .quantize import quantize_act_1x128, quantize_act_1x128_t, quantize_w_128x128
+from .quantize import (quantize_act_1x128, quantize_act_1x128_t, quantize_w_128x128, dequantize_act_1x128,
+                       requantize_act_1x128_t)
 from .gemm import gemm_fprop, gemm_dgrad, gemm_wgrad, grouped_gemm, gemm_dequant_reference
 from .moe import moe_max_rows, moe_route, moe_permute_quantize, moe_combine, moe_combine_exact
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode_table", "e4m3_decode", "e4m3_encode",
     "bf16_to_f32", "f32_to_bf16_rne", "f64_to_bf16_rne",
-    "quantize_act_1x128", "quantize_act_1x128_t", "quantize_w_128x128",
+    "quantize_act_1x128", "quantize_act_1x128_t", "quantize_w_128x128", "dequantize_act_1x128",
+    "requantize_act_1x128_t",
     "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "grouped_gemm", "gemm_dequant_reference",
     "moe_max_rows", "moe_route", "moe_permute_quantize", "moe_combine", "moe_combine_exact",
 ]

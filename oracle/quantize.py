@@ -19,12 +19,23 @@ to a power of two.  Layouts are row-major:
     activation tiles   x [R, C] -> q [R, C],  s [R, C/128]
     transposed tiles   x [T, C] -> q [C, T],  s [C, T/128]  (tiles run along T)
     weight blocks      w [N, K] -> q [N, K],  s [N/128, K/128]
+
+FP8 activation caching (deepseek.csdn.net page, section 二(四), and the
+qqstock.cn page, FP8 section: activations are stored in FP8 for the backward
+pass).  The cached form of x [T, C] is the forward's own 1x128 tiles
+(q [T, C], s [T, C/128]); the weight gradient needs tiles along T, so the
+backward re-tiles from the cache (the pages do not say how; plainest reading):
+    x_hat[t, c] = fl32(s[t, c/128] * dec(q[t, c]))     (one binary32 multiply)
+    then the transposed tile quantizer above, applied to x_hat as binary32
+    values (amax, fl32(amax/448), fl32(x_hat/s'), E4M3 RNE with saturation).
+The value is rounded twice (once to E4M3 in the forward tiles, once in the
+tiles along T); this composition is the definition.
 """
 
 import numpy as np
 
 from .bf16 import bf16_to_f32
-from .e4m3 import E4M3_MAX, e4m3_encode
+from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode
 
 GROUP = 128
 
@@ -83,3 +94,24 @@ def quantize_w_128x128(w_bits):
     q, s = _quantize_groups(blocks)
     q = q.reshape(nb, kb, GROUP, GROUP).transpose(0, 2, 1, 3).reshape(n, k)
     return np.ascontiguousarray(q), s.reshape(nb, kb)
+
+
+def dequantize_act_1x128(q, s):
+    """Cached 1x128 tiles back to binary32: x_hat [R, C] = fl32(s[r, c/128] * dec(q[r, c]))."""
+    q = np.asarray(q, dtype=np.uint8)
+    s = np.asarray(s, dtype=np.float32)
+    if q.ndim != 2 or q.shape[1] % GROUP or s.shape != (q.shape[0], q.shape[1] // GROUP):
+        raise ValueError("dequantize_act_1x128: need q [R, C] (C % 128 == 0) and s [R, C/128]")
+    dec = e4m3_decode(q).astype(np.float32)              # exact: every E4M3 value is a binary32
+    return (dec * np.repeat(s, GROUP, axis=1)).astype(np.float32)   # binary32 multiply, RN
+
+
+def requantize_act_1x128_t(q, s):
+    """Tiles along the rows of a cached activation: codes [C, T], scales [C, T/128] (T % 128 == 0)."""
+    x_hat = dequantize_act_1x128(q, s)
+    t, c = x_hat.shape
+    if t % GROUP:
+        raise ValueError("requantize_act_1x128_t: need T % 128 == 0")
+    xt = np.ascontiguousarray(x_hat.T)
+    qt, st = _quantize_groups(xt.reshape(c, t // GROUP, GROUP))
+    return qt.reshape(c, t), st.reshape(c, t // GROUP)
