@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
     "gemm": ["fp8_fine_grained_act_amd/csrc/gemm.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
     "quant": ["fp8_fine_grained_act_amd/csrc/quantize.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
     "moe": ["fp8_fine_grained_act_amd/csrc/moe.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
+    "requant": ["fp8_fine_grained_act_amd/csrc/requant.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
 }
 
 
@@ -56,6 +57,9 @@ def parse_args():
     p.add_argument("--eager", action="store_true", help="time eager launches instead of step graphs")
     p.add_argument("--separate-quant", action="store_true",
                    help="quantize each activation orientation with its own call instead of the fused call")
+    p.add_argument("--act-cache", action="store_true",
+                   help="FP8 activation caching (c2, c3, c5): X is kept as its forward 1x128 tiles and the "
+                        "weight gradient's tiles along the tokens are re-tiled from them")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 512 MiB device-to-device copies (reference for HBM byte counters)")
     return p.parse_args()
@@ -83,7 +87,7 @@ class Call:
         self.times_ms = []
 
 
-def build_layer_step(lib, cfg_name, rotate, dual=True):
+def build_layer_step(lib, cfg_name, rotate, dual=True, act_cache=False):
     """Calls of one training pass of a linear layer (configs c2 / c3 shapes).
 
     With ``dual`` (default) X and dY are each quantized once into both
@@ -119,7 +123,27 @@ def build_layer_step(lib, cfg_name, rotate, dual=True):
 
     act_bytes = lambda r, c: r * c * 3 + r * c // 128 * 4  # noqa: E731
     dual_bytes = lambda r, c: r * c * 4 + 2 * (r * c // 128) * 4  # noqa: E731
-    if dual:
+    requant_bytes = lambda r, c: r * c * 2 + 2 * (r * c // 128) * 4  # noqa: E731
+    if act_cache:
+        calls = [
+            Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(cur()[0], q=qx, scales=sx),
+                 nbytes=act_bytes(m, k), outs=(qx, sx)),
+            Call("quant_w", "quant", lambda: lib.fp8bs_quantize_w_128x128(cur()[1], q=qw, scales=sw),
+                 nbytes=n * k * 3 + (n // 128) * (k // 128) * 4, outs=(qw, sw)),
+            Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k,
+                 outs=(y,)),
+            Call("quant_act_dy_dual", "quant",
+                 lambda: lib.fp8bs_quantize_act_1x128_dual(cur()[2], q=qdy, scales=sdy, qt=qdyt, scales_t=sdyt),
+                 nbytes=dual_bytes(m, n), outs=(qdy, sdy, qdyt, sdyt)),
+            Call("gemm_dgrad", "gemm", lambda: lib.fp8bs_gemm(qdy, sdy, qw, sw, b_layout=1, c=dx),
+                 flops=2.0 * m * n * k, outs=(dx,)),
+            Call("requant_x_t", "requant",
+                 lambda: lib.fp8bs_requantize_act_1x128_t(qx, sx, qt=qxt, scales_t=sxt),
+                 nbytes=requant_bytes(m, k), outs=(qxt, sxt)),
+            Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdyt, sdyt, qxt, sxt, c=dw),
+                 flops=2.0 * m * n * k, outs=(dw,)),
+        ]
+    elif dual:
         calls = [
             Call("quant_act_x_dual", "quant",
                  lambda: lib.fp8bs_quantize_act_1x128_dual(cur()[0], q=qx, scales=sx, qt=qxt, scales_t=sxt),
@@ -160,7 +184,9 @@ def build_layer_step(lib, cfg_name, rotate, dual=True):
     desc = dict(workload=f"{cfg_name}: one FP8 training pass (forward + dgrad + wgrad, all quantization "
                          f"included) of a linear layer, {cfg['desc']}",
                 M_tokens=m, N_out=n, K_in=k, input_copies=rotate,
-                activation_quantization="one call per tensor for both orientations" if dual
+                activation_quantization=("X: forward 1x128 tiles kept as the FP8 cache, weight-gradient tiles "
+                                         "re-tiled from it; dY: one call for both orientations") if act_cache
+                else "one call per tensor for both orientations" if dual
                 else "one call per tensor and orientation")
     return calls, state, desc, d
 
@@ -236,7 +262,7 @@ def build_grouped_step(lib, rotate):
     return calls, state, desc, None
 
 
-def build_wgrad_step(lib, rotate):
+def build_wgrad_step(lib, rotate, act_cache=False):
     import torch
 
     from workloads import config_by_name, wgrad_inputs
@@ -251,16 +277,26 @@ def build_wgrad_step(lib, rotate):
         (n, t // 128), dtype=torch.float32, device="cuda")
     dw = torch.empty((m, n), dtype=torch.float32, device="cuda")
     state = {"i": 0}
+    if act_cache:
+        # the cached forward tiles of X exist before the step (the forward pass made them)
+        cx, csx = lib.fp8bs_quantize_act_1x128(x)
+        x_call = Call("requant_x_t", "requant",
+                      lambda: lib.fp8bs_requantize_act_1x128_t(cx, csx, qt=qx, scales_t=sx),
+                      nbytes=t * n * 2 + 2 * (t * n // 128) * 4, outs=(qx, sx))
+    else:
+        x_call = Call("quant_act_x_t", "quant",
+                      lambda: lib.fp8bs_quantize_act_1x128(x, transpose=1, q=qx, scales=sx),
+                      nbytes=t * n * 3 + t * n // 128 * 4, outs=(qx, sx))
     calls = [
         Call("quant_act_dy_t", "quant", lambda: lib.fp8bs_quantize_act_1x128(dy, transpose=1, q=qdy, scales=sdy),
              nbytes=t * m * 3 + t * m // 128 * 4, outs=(qdy, sdy)),
-        Call("quant_act_x_t", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, transpose=1, q=qx, scales=sx),
-             nbytes=t * n * 3 + t * n // 128 * 4, outs=(qx, sx)),
+        x_call,
         Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdy, sdy, qx, sx, c=dw), flops=2.0 * m * n * t,
              outs=(dw,)),
     ]
-    desc = dict(workload="c5: weight gradient dW[1536,7168] = dY^T X over 16384 tokens, both operands "
-                         "transpose-quantized along tokens", T=t, M=m, N=n)
+    desc = dict(workload="c5: weight gradient dW[1536,7168] = dY^T X over 16384 tokens, " + (
+                    "dY transpose-quantized along tokens, X re-tiled along tokens from its cached FP8 forward tiles"
+                    if act_cache else "both operands transpose-quantized along tokens"), T=t, M=m, N=n)
     return calls, state, desc, None
 
 
@@ -431,11 +467,14 @@ def main():
         return
 
     if args.config in ("c2", "c3"):
-        calls, state, desc, data = build_layer_step(lib, args.config, args.rotate, dual=not args.separate_quant)
+        calls, state, desc, data = build_layer_step(lib, args.config, args.rotate, dual=not args.separate_quant,
+                                                    act_cache=args.act_cache)
     elif args.config == "c4":
         calls, state, desc, data = build_grouped_step(lib, args.rotate)
     else:
-        calls, state, desc, data = build_wgrad_step(lib, args.rotate)
+        calls, state, desc, data = build_wgrad_step(lib, args.rotate, act_cache=args.act_cache)
+    if args.act_cache:
+        data = None                      # the CPU baseline times the plain pass only
     torch.cuda.synchronize()
     rotate = desc.get("input_copies", 1)
     run_steps(calls, state, 1)                       # first launches outside any capture

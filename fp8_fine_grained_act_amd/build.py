@@ -7,7 +7,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8bs.so")
-SOURCES = ["quantize.hip", "gemm.hip", "moe.hip"]
+SOURCES = ["quantize.hip", "requant.hip", "gemm.hip", "moe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

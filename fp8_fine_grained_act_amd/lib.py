@@ -25,6 +25,7 @@ _SIGNATURES = {
     "fp8bs_quantize_act_1x128_dual": [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _i64,
                                       _c_void_p, _c_void_p],
     "fp8bs_quantize_w_128x128": [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p],
+    "fp8bs_requantize_act_1x128_t": [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p],
     "fp8bs_gemm": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int, _c_void_p, _i64,
                    _c_void_p],
     "fp8bs_grouped_gemm": [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64, _i64,
@@ -149,6 +150,31 @@ def fp8bs_quantize_act_1x128_dual(x, q=None, scales=None, qt=None, scales_t=None
                                            qt.data_ptr(), ldqt, scales_t.data_ptr(), _stream(stream))
     _check("fp8bs_quantize_act_1x128_dual", st)
     return q, scales, qt, scales_t
+
+
+def fp8bs_requantize_act_1x128_t(q, scales, qt=None, scales_t=None, stream=None):
+    """Tiles along the rows from a cached activation: q [rows, cols] + scales [rows, cols/128]
+    -> qt [cols, rows], scales_t [cols, rows/128]."""
+    _dev(q, torch.uint8, "q")
+    ldq = _row_major(q, "q")
+    _dev(scales, torch.float32, "scales")
+    rows, cols = q.shape
+    if tuple(scales.shape) != (rows, cols // GROUP) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous [rows, cols/128] tensor")
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=q.device)
+    if scales_t is None:
+        scales_t = torch.empty((cols, rows // GROUP), dtype=torch.float32, device=q.device)
+    _dev(qt, torch.uint8, "qt")
+    ldqt = _row_major(qt, "qt")
+    _dev(scales_t, torch.float32, "scales_t")
+    if tuple(qt.shape) != (cols, rows) or tuple(scales_t.shape) != (cols, rows // GROUP) \
+            or not scales_t.is_contiguous():
+        raise ValueError("output shapes do not match the input")
+    st = raw.fp8bs_requantize_act_1x128_t(q.data_ptr(), scales.data_ptr(), rows, cols, ldq, qt.data_ptr(), ldqt,
+                                          scales_t.data_ptr(), _stream(stream))
+    _check("fp8bs_requantize_act_1x128_t", st)
+    return qt, scales_t
 
 
 def fp8bs_quantize_w_128x128(w, q=None, scales=None, stream=None):

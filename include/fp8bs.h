@@ -99,6 +99,30 @@ int fp8bs_quantize_act_1x128_dual(const uint16_t* x, int64_t rows, int64_t cols,
                                   int64_t ldqt, float* scales_t, void* stream);
 
 /*
+ * Re-tiling of a cached FP8 activation along its rows.  Activations are kept
+ * in FP8 for the backward pass (deepseek.csdn.net page, section 二(四);
+ * qqstock.cn page, FP8 section); the weight gradient contracts over the
+ * tokens, so it needs tiles along the rows, made here from the cache alone
+ * (the bf16 activation is no longer needed):
+ *   x_hat[t, c] = fl32(scales[t, c/128] * dec(q[t, c]))   (binary32 multiply)
+ *   qt, scales_t = the transpose == 1 tiles of x_hat, with the same rules
+ *   applied to the binary32 values (amax, s' = fl32(amax/448), E4M3
+ *   nearest-even of the binary32 quotient |x_hat| / s', sign kept; s' = 0
+ *   gives signed zeros).  The value is rounded twice: once in the forward
+ *   tiles, once here (a reading: the pages do not say how the cache is
+ *   re-tiled).
+ *   q         E4M3 [rows, cols], row stride ldq bytes (1x128 tiles along cols)
+ *   scales    f32  [rows, cols/128], contiguous
+ *   qt        E4M3 [cols, rows], row stride ldqt bytes (tiles along rows)
+ *   scales_t  f32  [cols, rows/128], contiguous
+ *   rows % 128 == 0, cols % 128 == 0.
+ * Alignment: q and qt 16 bytes, ldq % 16 == 0, ldqt % 16 == 0, scales and
+ * scales_t 4 bytes.  Outputs must not overlap the inputs.
+ */
+int fp8bs_requantize_act_1x128_t(const uint8_t* q, const float* scales, int64_t rows, int64_t cols,
+                                 int64_t ldq, uint8_t* qt, int64_t ldqt, float* scales_t, void* stream);
+
+/*
  * Weight quantization in 128x128 blocks (the pages' weight granularity).
  *   w       bf16 [n, k], row stride ldw elements
  *   q       E4M3 [n, k], row stride ldq bytes

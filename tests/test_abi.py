@@ -32,6 +32,7 @@ def test_header_declares_the_five_calls():
     names = declared_functions()
     for n in ("fp8bs_quantize_act_1x128", "fp8bs_quantize_w_128x128", "fp8bs_gemm", "fp8bs_grouped_gemm",
               "fp8bs_gemm_wgrad", "fp8bs_status_string", "fp8bs_moe_max_rows", "fp8bs_moe_route",
+              "fp8bs_requantize_act_1x128_t",
               "fp8bs_moe_permute_quantize", "fp8bs_moe_combine"):
         assert n in names
 
@@ -170,3 +171,15 @@ def test_moe_combine_validation(raw):
     assert f(P, 7172, 4096, P, P, 100, 8, 7168, P, 7168, None) == EALIGN      # ldy % 8
     assert f(P_ODD, 7168, 4096, P, P, 100, 8, 7168, P, 7168, None) == EALIGN
     assert f(P, 7168, 4096, P, P, 0, 8, 7168, P, 7168, None) == OK            # no tokens: nothing to do
+
+
+def test_requantize_act_t_validation(raw):
+    f = raw.fp8bs_requantize_act_1x128_t
+    assert f(P, None, 256, 256, 256, P, 256, P, None) == ENULL
+    assert f(P, P, 200, 256, 256, P, 256, P, None) == ESHAPE          # rows % 128
+    assert f(P, P, 256, 200, 208, P, 256, P, None) == ESHAPE          # cols % 128
+    assert f(P, P, 256, 256, 128, P, 256, P, None) == ESHAPE          # ldq < cols
+    assert f(P, P, 256, 256, 256, P, 128, P, None) == ESHAPE          # ldqt < rows
+    assert f(P, P, 256, 256, 264, P, 256, P, None) == EALIGN          # ldq % 16
+    assert f(P_ODD, P, 256, 256, 256, P, 256, P, None) == EALIGN
+    assert f(P, P, 0, 256, 256, P, 256, P, None) == ESHAPE

@@ -32,3 +32,19 @@ def test_reciprocal_correction_matches_ieee_division_exhaustively(tmp_path):
     out = subprocess.run([str(exe), hex(thr)], capture_output=True, text=True, timeout=600)
     assert out.returncode == 0, out.stdout + out.stderr
     assert out.stdout.count("mismatches=0") == 2, out.stdout
+
+
+REQUANT_SRC = os.path.join(HERE, "host", "requant_division_check.c")
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_retiling_quotient_matches_ieee_division_near_every_boundary(tmp_path):
+    """The re-tiling kernel divides arbitrary binary32 values (s * dec(q)), which the
+    exhaustive bf16 enumeration does not cover: check its quotient sequence against the
+    IEEE quotient for numerators within 6 ulps of every E4M3 rounding boundary, for
+    divisors spread over every binary32 binade (normal and subnormal)."""
+    exe = tmp_path / "requant_division_check"
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-o", str(exe), REQUANT_SRC, "-lm"], check=True)
+    out = subprocess.run([str(exe), "96"], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "mismatches=0" in out.stdout, out.stdout
