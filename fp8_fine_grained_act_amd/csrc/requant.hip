@@ -19,8 +19,9 @@
 // those of the IEEE quotient for numerators within a few ulps of every E4M3
 // rounding boundary, for divisors in every binade.
 //
-// One 256-thread workgroup per 128 x 128 square.  The square's codes (16 KB)
-// are staged in LDS; lane (g, j) (g = tid / 8, j = tid % 8) then owns columns
+// One 256-thread workgroup per 128 x 128 square.  The square's codes (16 KB,
+// read once: non-temporal loads, 19.6 -> 18.3 us on 4096 x 7168) are staged
+// in LDS; lane (g, j) (g = tid / 8, j = tid % 8) then owns columns
 // 4g..4g+3 and tokens 16j..16j+15: one 4-byte LDS read per token gives its
 // four columns, a column's amax is a max over the 8 lanes of the group (DPP),
 // and for each column the group's 8 lanes store its whole 128-byte output
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(256) void requant_t_kernel(const uint8_t* __restric
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = tid + 256 * j, r = i >> 3, ch = i & 7;
-    const uint4 v = *reinterpret_cast<const uint4*>(q + (t0 + r) * ldq + c0 + 16 * ch);
+    const uint4 v = load_nt(q + (t0 + r) * ldq + c0 + 16 * ch);
     *reinterpret_cast<uint4*>(tile + req_dw(r, 4 * ch)) = v;
   }
   if (tid < 128) rs[req_rs(tid)] = s[(t0 + tid) * cblocks + cb];
@@ -83,7 +84,8 @@ __global__ __launch_bounds__(256) void requant_t_kernel(const uint8_t* __restric
     const float amax = __uint_as_float(max8_u32(__float_as_uint(am[b])));
     const float sp = amax / kE4M3Max;
     const bool tiny = amax < kReqTinyAmax;
-    const float d = tiny ? sp * kTinyScale : sp;
+    const float up = tiny ? kTinyScale : 1.0f;         // exact scaling of numerator and divisor
+    const float d = sp * up;
     const float rcp = d == 0.0f ? 0.0f : 1.0f / d;
     uint32_t packed[4];
 #pragma unroll
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void requant_t_kernel(const uint8_t* __restric
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x = xh[b][4 * k + e];
-        const float a = tiny ? fabsf(x) * kTinyScale : fabsf(x);
+        const float a = fabsf(x) * up;
         const float q0 = a * rcp;
         const float err = __builtin_fmaf(-q0, d, a);
         qv[e] = __builtin_fmaf(err, rcp, q0);
