@@ -45,7 +45,7 @@ brute force, textbook special cases).  No function here is "parity unpinned".
 from .e4m3 import E4M3_MAX, e4m3_decode_table, e4m3_decode, e4m3_encode
 from .bf16 import bf16_to_f32, f32_to_bf16_rne, f64_to_bf16_rne
 from .quantize import (quantize_act_1x128, quantize_act_1x128_t, quantize_w_128x128, dequantize_act_1x128,
-                       requantize_act_1x128_t)
+                       requantize_act_1x128_t, quantize_per_tensor)
 from .gemm import gemm_fprop, gemm_dgrad, gemm_wgrad, grouped_gemm, gemm_dequant_reference
 from .moe import moe_max_rows, moe_route, moe_permute_quantize, moe_combine, moe_combine_exact
 
@@ -53,7 +53,7 @@ __all__ = [
     "E4M3_MAX", "e4m3_decode_table", "e4m3_decode", "e4m3_encode",
     "bf16_to_f32", "f32_to_bf16_rne", "f64_to_bf16_rne",
     "quantize_act_1x128", "quantize_act_1x128_t", "quantize_w_128x128", "dequantize_act_1x128",
-    "requantize_act_1x128_t",
+    "requantize_act_1x128_t", "quantize_per_tensor",
     "gemm_fprop", "gemm_dgrad", "gemm_wgrad", "grouped_gemm", "gemm_dequant_reference",
     "moe_max_rows", "moe_route", "moe_permute_quantize", "moe_combine", "moe_combine_exact",
 ]

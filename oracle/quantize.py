@@ -115,3 +115,12 @@ def requantize_act_1x128_t(q, s):
     xt = np.ascontiguousarray(x_hat.T)
     qt, st = _quantize_groups(xt.reshape(c, t // GROUP, GROUP))
     return qt.reshape(c, t), st.reshape(c, t // GROUP)
+
+
+def quantize_per_tensor(x_bits):
+    """One scale for the whole tensor: the scaling that the 1x128 / 128x128 groups replace
+    (qqstock.cn page, FP8 section).  The same rules with a single group: amax over the
+    tensor, s = fl32(amax/448), codes of fl32(x/s).  Returns (codes, float32 scalar scale)."""
+    x = bf16_to_f32(x_bits)
+    q, s = _quantize_groups(x.reshape(1, -1))
+    return q.reshape(x.shape), np.float32(s[0])
