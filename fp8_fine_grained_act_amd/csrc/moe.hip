@@ -15,7 +15,7 @@
 //   moe_route_rows_kernel  each row's token
 //   moe_dispatch_kernel  each token row is read once, coded once in 1x128
 //                        tiles and its codes and scales stored to its k rows;
-//                        one workgroup per expert zeroes its padding rows
+//                        four workgroups per expert zero its padding rows
 //   moe_combine_kernel   one wave per token: the gate-weighted FP32 sum of the
 //                        token's k expert-output rows, rounded once to bf16
 //
@@ -32,7 +32,7 @@
 namespace fp8bs {
 
 constexpr int kRouteWaves = 16;            // one 1024-thread workgroup
-constexpr int kRouteMaxExperts = 512;       // LDS: 96 KB of per-wave tables
+constexpr int kRouteMaxExperts = 512;      // LDS: 96 KB of per-wave tables
 constexpr int kMaxTopk = 64;               // a token's slots fit in one wave's lanes
 
 // ---------------------------------------------------------------------------
