@@ -240,3 +240,27 @@ def test_dispatch_grouped_combine_chain(gpu_lib, n):
     assert np.all(got[:total][~real] == 0) and np.all(got[total:] == 77.0)
     # the combine of the GPU's expert outputs against the oracle's combine of the same outputs
     _check_combine(bf16_bits_host(out), bf16_bits_host(y), r["slot_rows"], d["gates"], "chain: combine")
+
+
+def test_route_large_batch_and_most_experts(gpu_lib):
+    """16384 tokens x top-8 over 512 experts (131072 pairs: several 1024-pair batches per wave)."""
+    d = moe_dispatch_inputs({"tokens": 16384, "topk": 8, "experts": 512, "zipf_s": 0.8, "seed": 41, "K": 128})
+    _check_route(gpu_lib, d["ids"], 512, "16384 tokens, top-8 of 512")
+
+
+def test_combine_token_with_every_slot_dropped_is_zero(gpu_lib):
+    rng = np.random.default_rng(51)
+    y = normal_bf16(rng, (64, 136), 1.0)
+    slot = rng.integers(0, 64, size=(10, 4))
+    slot[3] = -1                                               # token 3: no expert row at all
+    slot[7, :2] = 1000                                         # rows past the capacity: dropped too
+    g = rng.uniform(0.1, 1.0, size=(10, 4)).astype(np.float32)
+    out = bf16_bits_host(gpu_lib.fp8bs_moe_combine(to_dev_bf16(y), to_dev(slot.astype(np.int32)), to_dev(g)))
+    assert np.all(out[3] == 0)
+    ref_slot = np.where(slot >= 64, -1, slot)
+    _check_combine(out, y, ref_slot, g, "dropped slots")
+
+
+def test_dispatch_wide_rows(gpu_lib):
+    """hidden 14336 (112 tiles: 14 wave steps per token), top-2 of 3 experts."""
+    _payload_case(gpu_lib, 40, 2, 3, 14336, 61)

@@ -106,3 +106,14 @@ def test_full_layer_activation_sampled_channel_blocks(gpu_lib, name):
     # three independent E4M3 roundings (forward tiles, re-tiling, direct tiles), each about
     # 2^-4/sqrt(3) relative RMS: about 0.047 together
     assert rel < 0.06
+
+
+def test_tall_and_narrow_caches(gpu_lib):
+    """65536 tokens x 128 channels (512 squares down one channel block) and 128 x 8192."""
+    rng = np.random.default_rng(71)
+    for t, c in ((65536, 128), (128, 8192)):
+        q, s = _random_cache(rng, t, c)
+        qt, st = gpu_lib.fp8bs_requantize_act_1x128_t(to_dev(q), to_dev(s))
+        torch.cuda.synchronize()
+        q_ref, s_ref = requantize_act_1x128_t(q, s)
+        _same(f"{t}x{c}", qt.cpu().numpy(), st.cpu().numpy(), q_ref, s_ref)
