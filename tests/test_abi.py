@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -183,3 +184,12 @@ def test_requantize_act_t_validation(raw):
     assert f(P, P, 256, 256, 264, P, 256, P, None) == EALIGN          # ldq % 16
     assert f(P_ODD, P, 256, 256, 256, P, 256, P, None) == EALIGN
     assert f(P, P, 0, 256, 256, P, 256, P, None) == ESHAPE
+
+
+def test_moe_max_rows_matches_the_oracle_bound(raw):
+    from oracle import moe_max_rows
+
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        t, k, e = int(rng.integers(0, 20000)), int(rng.integers(1, 65)), int(rng.integers(1, 65537))
+        assert raw.fp8bs_moe_max_rows(t, k, e) == moe_max_rows(t, k, e), (t, k, e)
