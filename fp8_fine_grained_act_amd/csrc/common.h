@@ -148,6 +148,11 @@ __device__ __forceinline__ void store_nt(void* p, uint4 v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
+__device__ __forceinline__ void store_nt(void* p, uint2 v) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
 __device__ __forceinline__ uint4 load_nt(const void* p) {
   const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(w.x, w.y, w.z, w.w);

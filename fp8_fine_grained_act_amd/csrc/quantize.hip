@@ -113,7 +113,12 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
   uint4 v[8];
   auto load = [&](int sq) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(src + ((int64_t)sq * kQB + 16 * i) * ldx);
+    for (int i = 0; i < 8; ++i) {
+      // transposed-only: x is read once, non-temporal (c5's X, 16384 x 7168:
+      // 78 -> 72 us); the fused kernel measured slower with the hint
+      const uint16_t* a = src + ((int64_t)sq * kQB + 16 * i) * ldx;
+      v[i] = ROWS ? *reinterpret_cast<const uint4*>(a) : load_nt(a);
+    }
     if (!cok) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = make_uint4(0, 0, 0, 0);
@@ -209,7 +214,9 @@ static bool cols_grid_ok(int64_t rows, int64_t cols) {
 // 128x128 weight blocks: w [n, k] -> q [n, k], s [n/128, k/128].
 // One 256-thread block per weight block; lane group of 16 covers one 256-byte
 // row segment, each thread holds 8 rows x 8 bf16 in registers between the amax
-// pass and the encode pass, so the block is read from HBM once.
+// pass and the encode pass, so the block is read from HBM once.  Weights and
+// codes pass through once: non-temporal loads and stores (1536 x 7168: 9.0 ->
+// 8.0 us; 32 experts of 4096 x 7168: 501-526 -> 486-498 us).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_w_kernel(
     const uint16_t* __restrict__ w, int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
   const uint16_t* base = w + (bn * 128 + rr) * ldw + bk * 128 + chunk * 8;
   uint4 v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(base + (int64_t)(16 * i) * ldw);
+  for (int i = 0; i < 8; ++i) v[i] = load_nt(base + (int64_t)(16 * i) * ldw);
 
   constexpr uint32_t kMag = 0x7FFF7FFFu;
   uint32_t m2 = 0;
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
   uint2 o[8];
   quant_run<32>(reinterpret_cast<const uint32_t*>(v), reinterpret_cast<uint32_t*>(o), g);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint2*>(dst + (int64_t)(16 * i) * ldq) = o[i];
+  for (int i = 0; i < 8; ++i) store_nt(dst + (int64_t)(16 * i) * ldq, o[i]);
   if (tid == 0) scales[blk] = g.s;
 }
 
