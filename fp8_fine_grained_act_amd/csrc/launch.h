@@ -20,6 +20,12 @@ inline int launch_status() {
   return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH;
 }
 
+// Inputs above this size are read (and, for weight codes, written) with the
+// non-temporal hint: at more than half of the 256 MB last-level cache they
+// are not expected to be found there, and the hint keeps them from evicting
+// data that is.  Smaller inputs may still be cached from their producer.
+constexpr int64_t kStreamBytes = 128LL << 20;
+
 // Compute units of the current device (cached per device; persistent grids
 // and tile-shape choices are sized by it).
 inline int cu_count() {

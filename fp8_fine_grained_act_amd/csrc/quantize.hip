@@ -89,7 +89,12 @@ __device__ __forceinline__ int qswz(int row) { return (row & 15) ^ (((row >> 5) 
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-template <bool ROWS>
+// STREAM: the input is larger than half the last-level cache, so it is read
+// with the non-temporal hint (cold 16384 x 7168: 78 -> 72 us); an input that fits
+// may still be cached from its producer, and the hint loses those hits
+// (warm 16384 x 1536: 14.7 -> 18.5 us).  The fused kernel is slower with the
+// hint in both cases and never streams.
+template <bool ROWS, bool STREAM = false>
 __global__ __launch_bounds__(256) void quant_act_cols_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t rows, int64_t cols,
     uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st,
@@ -114,10 +119,8 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
   auto load = [&](int sq) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // transposed-only: x is read once, non-temporal (c5's X, 16384 x 7168:
-      // 78 -> 72 us); the fused kernel measured slower with the hint
       const uint16_t* a = src + ((int64_t)sq * kQB + 16 * i) * ldx;
-      v[i] = ROWS ? *reinterpret_cast<const uint4*>(a) : load_nt(a);
+      v[i] = STREAM ? load_nt(a) : *reinterpret_cast<const uint4*>(a);
     }
     if (!cok) {
 #pragma unroll
@@ -214,10 +217,14 @@ static bool cols_grid_ok(int64_t rows, int64_t cols) {
 // 128x128 weight blocks: w [n, k] -> q [n, k], s [n/128, k/128].
 // One 256-thread block per weight block; lane group of 16 covers one 256-byte
 // row segment, each thread holds 8 rows x 8 bf16 in registers between the amax
-// pass and the encode pass, so the block is read from HBM once.  Weights and
-// codes pass through once: non-temporal loads and stores (1536 x 7168: 9.0 ->
-// 8.0 us; 32 experts of 4096 x 7168: 501-526 -> 486-498 us).
+// pass and the encode pass, so the block is read from HBM once.  STREAM (a
+// weight tensor larger than half the last-level cache, such as stacked experts):
+// weights and codes pass through with the non-temporal hint (32 experts of
+// 4096 x 7168: 501-526 -> 486-498 us); smaller tensors keep plain accesses, so
+// a weight still cached from its update is read from the cache and its codes
+// stay there for the GEMM that follows.
 // ---------------------------------------------------------------------------
+template <bool STREAM>
 __global__ __launch_bounds__(256) void quant_w_kernel(
     const uint16_t* __restrict__ w, int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
     float* __restrict__ scales, int64_t kblocks) {
@@ -232,7 +239,10 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
   const uint16_t* base = w + (bn * 128 + rr) * ldw + bk * 128 + chunk * 8;
   uint4 v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = load_nt(base + (int64_t)(16 * i) * ldw);
+  for (int i = 0; i < 8; ++i) {
+    const uint16_t* a = base + (int64_t)(16 * i) * ldw;
+    v[i] = STREAM ? load_nt(a) : *reinterpret_cast<const uint4*>(a);
+  }
 
   constexpr uint32_t kMag = 0x7FFF7FFFu;
   uint32_t m2 = 0;
@@ -249,7 +259,11 @@ __global__ __launch_bounds__(256) void quant_w_kernel(
   uint2 o[8];
   quant_run<32>(reinterpret_cast<const uint32_t*>(v), reinterpret_cast<uint32_t*>(o), g);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) store_nt(dst + (int64_t)(16 * i) * ldq, o[i]);
+  for (int i = 0; i < 8; ++i) {
+    uint8_t* d = dst + (int64_t)(16 * i) * ldq;
+    if (STREAM) store_nt(d, o[i]);
+    else *reinterpret_cast<uint2*>(d) = o[i];
+  }
   if (tid == 0) scales[blk] = g.s;
 }
 
@@ -278,8 +292,12 @@ extern "C" int fp8bs_quantize_act_1x128(const uint16_t* x, int64_t rows, int64_t
   } else {
     if (rows % kGroup || cols % 8 || ldq < rows) return FP8BS_ERR_SHAPE;
     if (!cols_grid_ok(rows, cols)) return FP8BS_ERR_SHAPE;
-    hipLaunchKernelGGL(quant_act_cols_kernel<false>, cols_grid(rows, cols), dim3(256), 0, s, x,
-                       ldx, rows, cols, q, ldq, scales, (uint8_t*)nullptr, (int64_t)0, (float*)nullptr);
+    if (rows * cols * 2 > kStreamBytes)
+      hipLaunchKernelGGL((quant_act_cols_kernel<false, true>), cols_grid(rows, cols), dim3(256), 0, s, x,
+                         ldx, rows, cols, q, ldq, scales, (uint8_t*)nullptr, (int64_t)0, (float*)nullptr);
+    else
+      hipLaunchKernelGGL((quant_act_cols_kernel<false, false>), cols_grid(rows, cols), dim3(256), 0, s, x,
+                         ldx, rows, cols, q, ldq, scales, (uint8_t*)nullptr, (int64_t)0, (float*)nullptr);
   }
   return launch_status();
 }
@@ -309,8 +327,12 @@ extern "C" int fp8bs_quantize_w_128x128(const uint16_t* w, int64_t n, int64_t k,
   const int64_t kb = k / kGroup;
   const int64_t blocks = (n / kGroup) * kb;
   if (blocks > kMaxGrid) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_w_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w,
-                     ldw, q, ldq, scales, kb);
+  if (n * k * 2 > kStreamBytes)
+    hipLaunchKernelGGL(quant_w_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w,
+                       ldw, q, ldq, scales, kb);
+  else
+    hipLaunchKernelGGL(quant_w_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w,
+                       ldw, q, ldq, scales, kb);
   return launch_status();
 }
 
