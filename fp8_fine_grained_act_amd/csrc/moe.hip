@@ -188,10 +188,10 @@ __global__ __launch_bounds__(256) void moe_route_rows_kernel(const int32_t* __re
 // zero rows are written alongside the token blocks rather than after them:
 // with a skewed routing padding is a large share of the rows (21120 of 53888
 // for 4096 tokens, top-8 of 256 experts, Zipf 1.1).  Each padding row (token
-// -1) gets +0 codes and scale 0.  The routed rows' codes are stored with the
-// non-temporal hint (measured at that size: 98 -> 72 us; the hint on the
-// padding rows' zeros made it slower, and so did placing the padding blocks
-// after the token blocks or giving a wave more than one token).
+// -1) gets +0 codes and scale 0.  STREAM: the routed rows' codes are stored
+// with the non-temporal hint (measured at that size: 98 -> 72 us; the hint
+// on the padding rows' zeros made it slower, and so did placing the padding
+// blocks after the token blocks or giving a wave more than one token).
 __device__ __forceinline__ uint32_t tile16_amax(const uint32_t in[8]) {
   constexpr uint32_t kMag = 0x7FFF7FFFu;
   const uint32_t m2 = max_u16x2(max_u16x2(max_u16x2(in[0] & kMag, in[1] & kMag), max_u16x2(in[2] & kMag, in[3] & kMag)),
@@ -201,7 +201,7 @@ __device__ __forceinline__ uint32_t tile16_amax(const uint32_t in[8]) {
 
 constexpr int kPadParts = 4;                        // padding workgroups per expert
 
-template <int TPW>
+template <int TPW, bool STREAM>
 __global__ __launch_bounds__(256) void moe_dispatch_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t tokens, int hidden,
     const int32_t* __restrict__ slot_rows, int topk, const int32_t* __restrict__ seg,
@@ -272,7 +272,9 @@ __global__ __launch_bounds__(256) void moe_dispatch_kernel(
         for (int j = 0; j < topk; ++j) {              // uniform loop: readlane sees every lane
           const int row = __builtin_amdgcn_readlane(my_row[u], j);
           if (row < 0 || g >= groups) continue;
-          store_nt(q + (int64_t)row * ldq + (int64_t)g * kGroup + 16 * sg, o);
+          uint8_t* d = q + (int64_t)row * ldq + (int64_t)g * kGroup + 16 * sg;
+          if (STREAM) store_nt(d, o);
+          else *reinterpret_cast<uint4*>(d) = o;
           if (sg == 0) scales[(int64_t)row * groups + g] = gs.s;
         }
         a[u] = na[u];
@@ -288,10 +290,10 @@ __global__ __launch_bounds__(256) void moe_dispatch_kernel(
 // slots at a time, then folded in slot order: acc = fma(g_j, y_j, acc) in
 // FP32, starting from +0; a dropped slot (row -1 or outside the capacity) is
 // skipped.  The sum is rounded once to bf16 (nearest, ties to even).
-// The expert rows are read once, with the non-temporal hint (measured on
-// 4096 tokens x top-8, 7168 columns: 110 -> 98.5 us; the hint on the output
-// store, or more tokens per wave, did not help).
-template <int TPW>
+// STREAM: the expert rows are read once, with the non-temporal hint
+// (measured on 4096 tokens x top-8, 7168 columns: 110 -> 98.5 us; the hint on
+// the output store, or more tokens per wave, did not help).
+template <int TPW, bool STREAM>
 __global__ __launch_bounds__(256) void moe_combine_kernel(
     const uint16_t* __restrict__ y, int64_t ldy, int64_t cap, const int32_t* __restrict__ slot_rows,
     const float* __restrict__ gates, int64_t tokens, int topk, int n, uint16_t* __restrict__ out,
@@ -328,7 +330,8 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(
         for (int jj = 0; jj < 8; ++jj) {
           rows[u][jj] = j0 + jj < topk ? __builtin_amdgcn_readlane(my_row[u], j0 + jj) : -1;
           v[u][jj] = rows[u][jj] >= 0 && live
-                         ? load_nt(y + (int64_t)rows[u][jj] * ldy + c)
+                         ? (STREAM ? load_nt(y + (int64_t)rows[u][jj] * ldy + c)
+                                   : *reinterpret_cast<const uint4*>(y + (int64_t)rows[u][jj] * ldy + c))
                          : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
@@ -414,9 +417,16 @@ extern "C" int fp8bs_moe_permute_quantize(const uint16_t* x, int64_t tokens, int
   const int64_t pad_blocks = num_experts * kPadParts;
   const int64_t grid = pad_blocks + token_blocks;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL(moe_dispatch_kernel<kDispatchTPW>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, x, ldx,
-                     tokens, (int)hidden, slot_rows, (int)topk, seg_offsets, row_token, q, ldq, scales, rows_cap,
-                     pad_blocks);
+  // the payload is streamed when it is larger than half the last-level cache;
+  // a smaller one stays cached for the grouped GEMM that reads it next
+  if (tokens * topk * hidden > kStreamBytes)
+    hipLaunchKernelGGL((moe_dispatch_kernel<kDispatchTPW, true>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, x, ldx, tokens, (int)hidden, slot_rows, (int)topk, seg_offsets, row_token,
+                       q, ldq, scales, rows_cap, pad_blocks);
+  else
+    hipLaunchKernelGGL((moe_dispatch_kernel<kDispatchTPW, false>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, x, ldx, tokens, (int)hidden, slot_rows, (int)topk, seg_offsets, row_token,
+                       q, ldq, scales, rows_cap, pad_blocks);
   return launch_status();
 }
 
@@ -433,7 +443,14 @@ extern "C" int fp8bs_moe_combine(const uint16_t* y, int64_t ldy, int64_t rows_ca
   if (tokens == 0) return FP8BS_OK;
   const int64_t grid = (tokens + 4 * kCombineTPW - 1) / (4 * kCombineTPW);
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL(moe_combine_kernel<kCombineTPW>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, y, ldy,
-                     rows_cap, slot_rows, gates, tokens, (int)topk, (int)n, out, ldo);
+  // the expert rows are streamed when they are larger than half the
+  // last-level cache; smaller ones may still be cached from the GEMM that
+  // produced them
+  if (tokens * topk * n * 2 > kStreamBytes)
+    hipLaunchKernelGGL((moe_combine_kernel<kCombineTPW, true>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, y, ldy, rows_cap, slot_rows, gates, tokens, (int)topk, (int)n, out, ldo);
+  else
+    hipLaunchKernelGGL((moe_combine_kernel<kCombineTPW, false>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, y, ldy, rows_cap, slot_rows, gates, tokens, (int)topk, (int)n, out, ldo);
   return launch_status();
 }
