@@ -401,3 +401,51 @@ def test_grouped_c4_full_launch_sampled_experts(gpu_lib):
         assert_gemm_parity(got[realm], c64[realm], mag[realm], label=f"c4 expert {e}")
         assert np.all(got[~realm] == 0)
     del w
+
+
+# --------------------------------------------------------- random shape sweep -----
+
+def _sweep_shapes(seed, count):
+    """Seeded shapes that cross the launch choices (small, 128x128, warp-specialized,
+    persistent, 128x192): M ragged, N and K multiples of 128."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(count):
+        m = int(rng.choice([rng.integers(1, 300), rng.integers(300, 3000), rng.integers(3000, 9000)]))
+        n = 128 * int(rng.integers(1, 64))
+        k = 128 * int(rng.integers(1, 24))
+        shapes.append((m, n, k))
+    return shapes
+
+
+@pytest.mark.parametrize("m,n,k", _sweep_shapes(301, 14))
+def test_forward_and_dgrad_shape_sweep(gpu_lib, m, n, k):
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    rows = _sample_rows(m, 6)
+    qa, sa = random_codes(rng, (m, k)), random_scales(rng, (m, k // 128))
+    qb, sb = random_codes(rng, (n, k)), random_scales(rng, (n // 128, k // 128))
+    got = bf16_values_host(gpu_lib.fp8bs_gemm(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb)))[rows]
+    c64 = gemm_fprop(qa[rows], sa[rows], qb, sb)
+    mag = gemm_fprop(magnitude_codes(qa[rows]), sa[rows], magnitude_codes(qb), sb)
+    assert_gemm_parity(got, c64, mag, label=f"fprop sweep {m}x{n}x{k}")
+    # dgrad: contraction n (as k here), weight stored [k_contr, n_out]
+    qw, sw = random_codes(rng, (k, n)), random_scales(rng, (k // 128, n // 128))
+    got = bf16_values_host(gpu_lib.fp8bs_gemm(to_dev(qa), to_dev(sa), to_dev(qw), to_dev(sw), b_layout=1))[rows]
+    c64 = gemm_dgrad(qa[rows], sa[rows], qw, sw)
+    mag = gemm_dgrad(magnitude_codes(qa[rows]), sa[rows], magnitude_codes(qw), sw)
+    assert_gemm_parity(got, c64, mag, label=f"dgrad sweep {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,t", [(s[0] % 2500 + 1, s[1] + 4 * (s[2] // 128 % 5), s[2]) for s in _sweep_shapes(302, 8)])
+def test_wgrad_shape_sweep(gpu_lib, m, n, t):
+    rng = np.random.default_rng(m + 11 * n + t)
+    qa, sa = random_codes(rng, (m, t)), random_scales(rng, (m, t // 128))
+    qb, sb = random_codes(rng, (n, t)), random_scales(rng, (n, t // 128))
+    out = gpu_lib.fp8bs_gemm_wgrad(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb))
+    torch.cuda.synchronize()
+    wr = _sample_rows(m, 6)
+    cols = np.unique(np.concatenate([_sample_rows(n, 48, seed=5), np.arange(max(0, n - 8), n)]))
+    got = out.cpu().numpy()[np.ix_(wr, cols)].astype(np.float64)
+    c64 = gemm_wgrad(qa[wr], sa[wr], qb[cols], sb[cols])
+    mag = gemm_wgrad(magnitude_codes(qa[wr]), sa[wr], magnitude_codes(qb[cols]), sb[cols])
+    assert_gemm_parity(got, c64, mag, out_bf16=False, label=f"wgrad sweep {m}x{n}x{t}")
