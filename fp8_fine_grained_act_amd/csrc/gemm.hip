@@ -172,6 +172,43 @@ struct GemmCfg {
   }
 };
 
+// bf16 output of one 16-row MFMA group.  The MFMA leaves lane (g, r)
+// (g = lane / 16, r = lane % 16) with columns 4g..4g+3 of output row r of
+// each 16x16 tile, so storing a tile as it stands writes four 8-byte pieces
+// per row.  Two adjacent tiles are stored together instead: a
+// v_permlane16_swap per register pair exchanges the first tile's odd
+// 16-lane groups with the second tile's even groups, after which lane g holds
+// 8 consecutive columns, 16 * (g % 2) + 8 * (g / 2) onwards, of the 32, and one
+// store instruction writes each row's 32 columns as 64 contiguous bytes
+// (dgrad 4096x7168x1536 71 -> 62 us, forward 4096x32768x512 142 -> 125 us).
+// An odd last tile is stored as it stands.  N is a multiple of 128 and c is
+// 16-byte aligned with ldc % 8 == 0, so each 8-column piece is whole and aligned.
+template <int TN, int TM>
+__device__ __forceinline__ void store_row_bf16(const GemmArgs& p, const v4f (&acc)[TN][TM], int j, int64_t row,
+                                               int64_t col0, int g) {
+  uint16_t* const crow = reinterpret_cast<uint16_t*>(p.c) + row * p.ldc;
+#pragma unroll
+  for (int i = 0; i + 1 < TN; i += 2) {
+    const uint32_t x0 = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+    const uint32_t x1 = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+    const uint32_t y0 = f32_to_bf16_rne(acc[i + 1][j][0]) | (f32_to_bf16_rne(acc[i + 1][j][1]) << 16);
+    const uint32_t y1 = f32_to_bf16_rne(acc[i + 1][j][2]) | (f32_to_bf16_rne(acc[i + 1][j][3]) << 16);
+    const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
+    const int64_t col = col0 + 16 * i + 16 * (g & 1) + 8 * (g >> 1);
+    if (col < p.n) *reinterpret_cast<uint4*>(crow + col) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+  }
+  if (TN % 2) {
+    const int64_t col = col0 + 16 * (TN - 1) + 4 * g;
+    if (col < p.n) {
+      uint2 o;
+      o.x = f32_to_bf16_rne(acc[TN - 1][j][0]) | (f32_to_bf16_rne(acc[TN - 1][j][1]) << 16);
+      o.y = f32_to_bf16_rne(acc[TN - 1][j][2]) | (f32_to_bf16_rne(acc[TN - 1][j][3]) << 16);
+      *reinterpret_cast<uint2*>(crow + col) = o;
+    }
+  }
+}
+
 template <int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void gemm_kernel(GemmArgs p) {
@@ -399,25 +436,21 @@ void gemm_kernel(GemmArgs p) {
   for (int j = 0; j < TM; ++j) {
     const int64_t row = m0 + WM * wm + 16 * j + l16;
     if (row >= M) continue;
+    if (MODE != kWgrad) {
+      store_row_bf16<TN, TM>(p, acc, j, row, n0 + WN * wn, g);
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       const int64_t col = n0 + WN * wn + 16 * i + 4 * g;
       if (col >= N) continue;
-      if (MODE == kWgrad) {
-        float* dst = reinterpret_cast<float*>(p.c) + row * p.ldc + col;
-        float4 o = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        if (p.accumulate) {
-          const float4 old = *reinterpret_cast<const float4*>(dst);
-          o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
-        }
-        *reinterpret_cast<float4*>(dst) = o;
-      } else {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + row * p.ldc + col;
-        uint2 o;
-        o.x = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
-        o.y = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(dst) = o;
+      float* dst = reinterpret_cast<float*>(p.c) + row * p.ldc + col;
+      float4 o = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      if (p.accumulate) {
+        const float4 old = *reinterpret_cast<const float4*>(dst);
+        o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
       }
+      *reinterpret_cast<float4*>(dst) = o;
     }
   }
 }
@@ -880,11 +913,13 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     for (int j = 0; j < TM; ++j) {
       const int64_t row = m0 + WM * wm + 16 * j + l16;
       if (row >= M) continue;
+      if (MODE != kWgrad) {
+        store_row_bf16<TN, TM>(p, acc, j, row, n0 + WN * wn, g);
+      } else {
 #pragma unroll
-      for (int i = 0; i < TN; ++i) {
-        const int64_t col = n0 + WN * wn + 16 * i + 4 * g;
-        if (col >= N) continue;
-        if (MODE == kWgrad) {
+        for (int i = 0; i < TN; ++i) {
+          const int64_t col = n0 + WN * wn + 16 * i + 4 * g;
+          if (col >= N) continue;
           float* dst = reinterpret_cast<float*>(p.c) + row * p.ldc + col;
           float4 o = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
           if (p.accumulate) {
@@ -892,12 +927,6 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
             o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
           }
           *reinterpret_cast<float4*>(dst) = o;
-        } else {
-          uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + row * p.ldc + col;
-          uint2 o;
-          o.x = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
-          o.y = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
-          *reinterpret_cast<uint2*>(dst) = o;
         }
       }
       __builtin_amdgcn_sched_barrier(0);     // one row of stores at a time: few live temporaries
