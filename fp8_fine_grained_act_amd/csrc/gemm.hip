@@ -767,14 +767,21 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // The head of a slab: what its first 16-row group needs (all B fragments,
-  // the first A fragment, the first row scale, the column scales).  It is read
-  // right after the barrier that publishes the slab, while the MFMAs of the
-  // previous slab's last group still run.
+  // The head of a slab: what its first 16-row groups need (all B fragments,
+  // the first two A fragments and row scales, the column scales).  A
+  // fragments are read two groups ahead of their MFMAs (one group, 3-4 MFMAs,
+  // is shorter than an LDS round trip under load).  With the early head the
+  // slab's A fragments and scales are read right after the barrier that
+  // publishes it, while the MFMAs of the previous slab's last group still
+  // run, and each B fragment (with its column scales) is read into the
+  // registers of the previous slab's fragment i right after that fragment's
+  // last MFMA, so the head is never held twice (this frees the registers the
+  // deeper A prefetch takes: forward 4096x1536x7168 52 -> 51 us, weight
+  // gradient over 16384 tokens 235 -> 228 us).
   struct Head {
     v8i bf[TN];
-    v8i a0;
-    float wa0;
+    v8i a0, a1;
+    float wa0, wa1;
     float wb0;      // forward / dgrad: one weight block covers the patch's columns
     float wbs[TN];  // or one per 16-column MFMA tile (kWbPerTile)
     v4f wb[TN];     // weight gradient: a scale per column
@@ -786,6 +793,8 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     h.bf[0] = MODE == kDgrad ? frag_b_tr(s.b, 0) : frag(s.b, b_lo, b_hi, 0);
     h.a0 = frag(s.a, a_lo, a_hi, 0);
     h.wa0 = s.sa[WM * wm + l16];
+    h.a1 = frag(s.a, a_lo, a_hi, TM > 1 ? 1 : 0);
+    h.wa1 = s.sa[WM * wm + (TM > 1 ? 16 : 0) + l16];
     if (MODE == kWgrad) {
 #pragma unroll
       for (int i = 0; i < TN; ++i) h.wb[i] = *reinterpret_cast<const v4f*>(&s.sb[WN * wn + 16 * i + 4 * g]);
@@ -805,7 +814,7 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   // LDS instructions of one head, spread over the MFMAs of the group that
   // reads it (issued all at once they queue behind each other and hold up
   // that group's MFMAs)
-  constexpr int kHeadReads = (MODE == kDgrad ? 4 * TN : 2 * TN) + 2 + 1 + (MODE == kWgrad || kWbPerTile ? TN : 1);
+  constexpr int kHeadReads = (MODE == kDgrad ? 4 * TN : 2 * TN) + 2 * (2 + 1) + (MODE == kWgrad || kWbPerTile ? TN : 1);
   constexpr int kHeadPerMfma = (kHeadReads + TN - 1) / TN;
   auto barrier = [&]() {
     asm volatile("" ::: "memory");
@@ -846,27 +855,34 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
 
   // Slab kb from stage s; the last group passes barrier kb + 1 (every LDS read
   // of slab kb has returned by then, so the copy waves may refill its stage)
-  // and reads the head of slab kb + 1 from stage sn.  After the final slab
-  // that head is never used.
+  // and reads the head of slab kb + 1 from stage sn (A fragments and scales
+  // first, then each B fragment after its last MFMA here).  After the final
+  // slab that head is never used.
   auto slab = [&](const Stage<BM, BN>& s, const Stage<BM, BN>& sn) {
     if (!kEarly) {
       barrier();
       hd = read_head(s);
     }
-    v8i a_cur = hd.a0;
-    float wa_cur = hd.wa0;
-    Head nx;
+    v8i a_cur = hd.a0, a_n1 = hd.a1;
+    float wa_cur = hd.wa0, wa_n1 = hd.wa1;
+    v8i na0 = a_cur, na1 = a_n1;
+    float nwa0 = 0.f, nwa1 = 0.f, nwb0 = 0.f;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      v8i a_nxt = a_cur;
-      float wa_nxt = wa_cur;
-      if (j + 1 < TM) {
-        a_nxt = frag(s.a, a_lo, a_hi, j + 1);
-        wa_nxt = s.sa[WM * wm + 16 * (j + 1) + l16];
-      } else if (kEarly) {
+      const bool last = j + 1 == TM;
+      v8i a_n2 = a_n1;
+      float wa_n2 = wa_n1;
+      if (j + 2 < TM) {
+        a_n2 = frag(s.a, a_lo, a_hi, j + 2);
+        wa_n2 = s.sa[WM * wm + 16 * (j + 2) + l16];
+      } else if (last && kEarly) {
         __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0): slab kb fully read
         barrier();
-        nx = read_head(sn);
+        na0 = frag(sn.a, a_lo, a_hi, 0);
+        nwa0 = sn.sa[WM * wm + l16];
+        nwb0 = (MODE == kWgrad || kWbPerTile) ? 0.f : sn.sb[WN * wn];
+        na1 = frag(sn.a, a_lo, a_hi, TM > 1 ? 1 : 0);
+        nwa1 = sn.sa[WM * wm + (TM > 1 ? 16 : 0) + l16];
       }
       const float wj = MODE == kWgrad ? wa_cur : wa_cur * hd.wb0;
 #pragma unroll
@@ -880,12 +896,14 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
         P_prev = P;
         pw = kWbPerTile ? wa_cur * hd.wbs[i] : wj;
         if (MODE == kWgrad) pwb = hd.wb[i];
+        if (kEarly && last) {                 // fragment i's last use: refill it for slab kb + 1
+          hd.bf[i] = frag(sn.b, b_lo, b_hi, i);
+          if (MODE == kWgrad) hd.wb[i] = *reinterpret_cast<const v4f*>(&sn.sb[WN * wn + 16 * i + 4 * g]);
+          else if (kWbPerTile) hd.wbs[i] = sn.sb[WN * wn + 16 * i];
+        }
       }
-      // per 16-row group: the LDS reads of the next group first, then per
-      // MFMA tile the MFMA and the fold of the previous tile; in the last
-      // group the head reads of the next slab go between the MFMAs
-      if (j + 1 < TM || !kEarly) {
-        if (j + 1 < TM) __builtin_amdgcn_sched_group_barrier(0x0100, 3, 0); // DS reads
+      if (!last || !kEarly) {
+        if (j + 2 < TM) __builtin_amdgcn_sched_group_barrier(0x0100, 3, 0); // DS reads
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);               // one MFMA
@@ -900,10 +918,18 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      a_cur = a_nxt;
-      wa_cur = wa_nxt;
+      a_cur = a_n1;
+      a_n1 = a_n2;
+      wa_cur = wa_n1;
+      wa_n1 = wa_n2;
     }
-    if (kEarly) hd = nx;
+    if (kEarly) {
+      hd.a0 = na0;
+      hd.a1 = na1;
+      hd.wa0 = nwa0;
+      hd.wa1 = nwa1;
+      hd.wb0 = nwb0;
+    }
   };
   // ---- tile end: fold the pending partial, store, start the next tile ------
   Origin org = tile_origin(0);
