@@ -38,11 +38,14 @@ METRIC = "block-scaled FP8 GEMM TFLOP/s and % of MI355X FP8 dense MFMA peak (1 G
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# the sources behind each kernel family's launches (the kernel file, the device
+# helpers, the launch constants): traffic counters taken on other sources are stale
+_SHARED = ["fp8_fine_grained_act_amd/csrc/common.h", "fp8_fine_grained_act_amd/csrc/launch.h"]
 KERNEL_SOURCES = {
-    "gemm": ["fp8_fine_grained_act_amd/csrc/gemm.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
-    "quant": ["fp8_fine_grained_act_amd/csrc/quantize.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
-    "moe": ["fp8_fine_grained_act_amd/csrc/moe.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
-    "requant": ["fp8_fine_grained_act_amd/csrc/requant.hip", "fp8_fine_grained_act_amd/csrc/common.h"],
+    "gemm": ["fp8_fine_grained_act_amd/csrc/gemm.hip"] + _SHARED,
+    "quant": ["fp8_fine_grained_act_amd/csrc/quantize.hip"] + _SHARED,
+    "moe": ["fp8_fine_grained_act_amd/csrc/moe.hip"] + _SHARED,
+    "requant": ["fp8_fine_grained_act_amd/csrc/requant.hip"] + _SHARED,
 }
 
 
