@@ -400,6 +400,30 @@ def time_kernels(calls, state, rotate, reps):
     return out
 
 
+def copy_rate_gbps(reps=8):
+    """A plain 512 MiB device-to-device copy (reads and writes 512 MiB), timed
+    with HIP events on the current stream: the HBM rate a streaming kernel can
+    reach on this GPU, beside the 8 TB/s specification."""
+    import torch
+
+    n = 512 * 2 ** 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    rate = 2 * n * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return rate
+
+
 def cpu_baseline(cfg_name, data, sample_rows, min_seconds=10.0):
     """The oracle, as it stands, on a bounded sample of the same workload (host cores).
 
@@ -526,6 +550,7 @@ def main():
         for c in calls:
             c.times_ms.append(ms_per_step / len(calls))
     kernel_sum_us = sum(c.times_ms[0] for c in calls) * 1e3
+    copy_gbps = copy_rate_gbps() if args.kernel_reps > 0 else None
 
     kernels = {}
     for c in calls:
@@ -537,6 +562,8 @@ def main():
         else:
             gb = c.nbytes / (avg * 1e-3) / 1e9
             ent.update(gbps=round(gb, 1), frac_hbm_peak=round(gb / HBM_PEAK_GBPS, 4))
+            if copy_gbps:
+                ent["frac_copy"] = round(gb / copy_gbps, 4)
         tr = load_traffic(f"{args.config}:{c.name}", c.kind)
         if tr is not None:
             ent["traffic"] = tr
@@ -574,6 +601,7 @@ def main():
         "timing": {"step": "eager launches on one stream" if graphs is None else "one HIP graph per step "
                    "(replay checked bit-identical to eager launches)", "kernel_sum_us": round(kernel_sum_us, 1),
                    "kernel_reps": args.kernel_reps},
+        "hbm_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
     }
     if not args.no_cpu_baseline and data is not None:
         out["cpu_baseline"] = cpu_baseline(args.config, data, args.cpu_sample_rows)
