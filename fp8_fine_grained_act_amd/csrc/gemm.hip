@@ -1003,10 +1003,14 @@ static int64_t persistent_grid(const GemmArgs& a, int cus) {
   return g;
 }
 
-// MFMA waves per workgroup: two per SIMD for the forward and dgrad GEMMs
-// (one wave's fold and LDS reads issue under the other's MFMAs: forward
-// 4096x1536x7168 61.5 -> 56.7 us); one per SIMD for the weight gradient,
-// whose 8-instruction fold per MFMA does not fit 168 VGPRs without spills.
+// MFMA waves per workgroup: two per SIMD for the forward and dgrad GEMMs on
+// 256x128 and 192x128 tiles (one wave's fold and LDS reads issue under the
+// other's MFMAs; with one wave of twice the patch they ran 9% slower); one
+// per SIMD for the weight gradient, whose 8-instruction fold per MFMA does
+// not fit 168 VGPRs without spills, and for the 128x192 forward tiles, whose
+// 64x96 patches read 29% less LDS per slab than two waves' 64x48 ones
+// (4096x1536x7168: 51.3 -> 49.9 us; with the single-slab A prefetch two
+// waves per SIMD had been faster, 61.5 against 56.7 us).
 template <int MODE, int MW>
 static int launch_wide(GemmArgs a, hipStream_t s, int cus) {
   a.tiles_n = (a.n + 191) / 192;
@@ -1037,7 +1041,7 @@ static int launch_gemm_ws(GemmArgs a, hipStream_t s, int cus) {
   constexpr int MW = MODE == kWgrad ? 4 : 8;
   const int64_t c256 = tile_cost(a.m, a.n, 256, 128, 100, cus), c192 = tile_cost(a.m, a.n, 192, 128, 110, cus);
   if (MODE == kFprop && tile_cost(a.m, a.n, 128, 192, 121, cus) < (c256 < c192 ? c256 : c192))
-    return launch_wide<kFprop, 8>(a, s, cus);
+    return launch_wide<kFprop, 4>(a, s, cus);
   a.tiles_n = (a.n + 127) / 128;
   const bool tall = c256 <= c192;
   a.tiles_m = tall ? (a.m + 255) / 256 : (a.m + 191) / 192;
