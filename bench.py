@@ -132,6 +132,11 @@ def build_layer_step(lib, cfg_name, rotate, dual=True, act_cache=False):
         return sets[state["i"] % rotate]
 
     act_bytes = lambda r, c: r * c * 3 + r * c // 128 * 4  # noqa: E731
+    # compulsory GEMM bytes: both operands' codes and scales, the output
+    wsc = (n // 128) * (k // 128) * 4
+    fprop_bytes = m * k + m * (k // 128) * 4 + n * k + wsc + m * n * 2
+    dgrad_bytes = m * n + m * (n // 128) * 4 + n * k + wsc + m * k * 2
+    wgrad_bytes = (n + k) * m + (n + k) * (m // 128) * 4 + n * k * 4
     dual_bytes = lambda r, c: r * c * 4 + 2 * (r * c // 128) * 4  # noqa: E731
     requant_bytes = lambda r, c: r * c * 2 + 2 * (r * c // 128) * 4  # noqa: E731
     if act_cache:
@@ -140,18 +145,18 @@ def build_layer_step(lib, cfg_name, rotate, dual=True, act_cache=False):
                  nbytes=act_bytes(m, k), outs=(qx, sx)),
             Call("quant_w", "quant", lambda: lib.fp8bs_quantize_w_128x128(cur()[1], q=qw, scales=sw),
                  nbytes=n * k * 3 + (n // 128) * (k // 128) * 4, outs=(qw, sw)),
-            Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k,
+            Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k, nbytes=fprop_bytes,
                  outs=(y,)),
             Call("quant_act_dy_dual", "quant",
                  lambda: lib.fp8bs_quantize_act_1x128_dual(cur()[2], q=qdy, scales=sdy, qt=qdyt, scales_t=sdyt),
                  nbytes=dual_bytes(m, n), outs=(qdy, sdy, qdyt, sdyt)),
             Call("gemm_dgrad", "gemm", lambda: lib.fp8bs_gemm(qdy, sdy, qw, sw, b_layout=1, c=dx),
-                 flops=2.0 * m * n * k, outs=(dx,)),
+                 flops=2.0 * m * n * k, nbytes=dgrad_bytes, outs=(dx,)),
             Call("requant_x_t", "requant",
                  lambda: lib.fp8bs_requantize_act_1x128_t(qx, sx, qt=qxt, scales_t=sxt),
                  nbytes=requant_bytes(m, k), outs=(qxt, sxt)),
             Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdyt, sdyt, qxt, sxt, c=dw),
-                 flops=2.0 * m * n * k, outs=(dw,)),
+                 flops=2.0 * m * n * k, nbytes=wgrad_bytes, outs=(dw,)),
         ]
     elif dual:
         calls = [
@@ -160,15 +165,15 @@ def build_layer_step(lib, cfg_name, rotate, dual=True, act_cache=False):
                  nbytes=dual_bytes(m, k), outs=(qx, sx, qxt, sxt)),
             Call("quant_w", "quant", lambda: lib.fp8bs_quantize_w_128x128(cur()[1], q=qw, scales=sw),
                  nbytes=n * k * 3 + (n // 128) * (k // 128) * 4, outs=(qw, sw)),
-            Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k,
+            Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k, nbytes=fprop_bytes,
                  outs=(y,)),
             Call("quant_act_dy_dual", "quant",
                  lambda: lib.fp8bs_quantize_act_1x128_dual(cur()[2], q=qdy, scales=sdy, qt=qdyt, scales_t=sdyt),
                  nbytes=dual_bytes(m, n), outs=(qdy, sdy, qdyt, sdyt)),
             Call("gemm_dgrad", "gemm", lambda: lib.fp8bs_gemm(qdy, sdy, qw, sw, b_layout=1, c=dx),
-                 flops=2.0 * m * n * k, outs=(dx,)),
+                 flops=2.0 * m * n * k, nbytes=dgrad_bytes, outs=(dx,)),
             Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdyt, sdyt, qxt, sxt, c=dw),
-                 flops=2.0 * m * n * k, outs=(dw,)),
+                 flops=2.0 * m * n * k, nbytes=wgrad_bytes, outs=(dw,)),
         ]
     else:
         calls = [
@@ -176,12 +181,12 @@ def build_layer_step(lib, cfg_name, rotate, dual=True, act_cache=False):
                  nbytes=act_bytes(m, k), outs=(qx, sx)),
             Call("quant_w", "quant", lambda: lib.fp8bs_quantize_w_128x128(cur()[1], q=qw, scales=sw),
                  nbytes=n * k * 3 + (n // 128) * (k // 128) * 4, outs=(qw, sw)),
-            Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k,
+            Call("gemm_fprop", "gemm", lambda: lib.fp8bs_gemm(qx, sx, qw, sw, c=y), flops=2.0 * m * n * k, nbytes=fprop_bytes,
                  outs=(y,)),
             Call("quant_act_dy", "quant", lambda: lib.fp8bs_quantize_act_1x128(cur()[2], q=qdy, scales=sdy),
                  nbytes=act_bytes(m, n), outs=(qdy, sdy)),
             Call("gemm_dgrad", "gemm", lambda: lib.fp8bs_gemm(qdy, sdy, qw, sw, b_layout=1, c=dx),
-                 flops=2.0 * m * n * k, outs=(dx,)),
+                 flops=2.0 * m * n * k, nbytes=dgrad_bytes, outs=(dx,)),
             Call("quant_act_dy_t", "quant",
                  lambda: lib.fp8bs_quantize_act_1x128(cur()[2], transpose=1, q=qdyt, scales=sdyt),
                  nbytes=act_bytes(m, n), outs=(qdyt, sdyt)),
@@ -189,7 +194,7 @@ def build_layer_step(lib, cfg_name, rotate, dual=True, act_cache=False):
                  lambda: lib.fp8bs_quantize_act_1x128(cur()[0], transpose=1, q=qxt, scales=sxt),
                  nbytes=act_bytes(m, k), outs=(qxt, sxt)),
             Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdyt, sdyt, qxt, sxt, c=dw),
-                 flops=2.0 * m * n * k, outs=(dw,)),
+                 flops=2.0 * m * n * k, nbytes=wgrad_bytes, outs=(dw,)),
         ]
     desc = dict(workload=f"{cfg_name}: one FP8 training pass (forward + dgrad + wgrad, all quantization "
                          f"included) of a linear layer, {cfg['desc']}",
@@ -252,7 +257,9 @@ def build_grouped_step(lib, rotate):
         Call("quant_w_experts", "quant", lambda: lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw),
              nbytes=num_e * n * k * 3 + num_e * (n // 128) * (k // 128) * 4, outs=(qw, sw)),
         Call("gemm_grouped", "gemm", lambda: lib.fp8bs_grouped_gemm(qx, sx, seg, qw, sw, c=y),
-             flops=2.0 * pairs * n * k, outs=(y,)),
+             flops=2.0 * pairs * n * k,
+             nbytes=pairs * (k + k // 128 * 4) + num_e * (n * k + (n // 128) * (k // 128) * 4) + pairs * n * 2,
+             outs=(y,)),
         Call("moe_combine", "moe", lambda: lib.fp8bs_moe_combine(y_down, slot, gates, out=out),
              nbytes=pairs * k * 2 + tokens * topk * 8 + tokens * k * 2, outs=(out,)),
     ]
@@ -302,6 +309,7 @@ def build_wgrad_step(lib, rotate, act_cache=False):
              nbytes=t * m * 3 + t * m // 128 * 4, outs=(qdy, sdy)),
         x_call,
         Call("gemm_wgrad", "gemm", lambda: lib.fp8bs_gemm_wgrad(qdy, sdy, qx, sx, c=dw), flops=2.0 * m * n * t,
+             nbytes=(m + n) * t + (m + n) * (t // 128) * 4 + m * n * 4,
              outs=(dw,)),
     ]
     desc = dict(workload="c5: weight gradient dW[1536,7168] = dY^T X over 16384 tokens, " + (
@@ -538,6 +546,10 @@ def main():
     wall = time.perf_counter() - t0
 
     ms_per_step = wall * 1e3 / args.steps
+    # the step's own roofline: per call, its FLOPs at the FP8 peak or its
+    # compulsory bytes at the HBM peak, whichever takes longer
+    roof_step_us = sum(max(c.flops / (FP8_PEAK_TFLOPS * 1e12), c.nbytes / (HBM_PEAK_GBPS * 1e9))
+                       for c in calls) * 1e6
     gemm_flops = sum(c.flops for c in calls)
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -593,6 +605,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "pct_of_fp8_dense_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
+        "step_roofline": {"us": round(roof_step_us, 1), "pct": round(100 * roof_step_us / (ms_per_step * 1e3), 1),
+                          "note": "per call max(FLOPs / 5 PFLOP/s, compulsory bytes / 8 TB/s), summed"},
         "dtype": "fp8_e4m3 (fp32 accumulate)",
         "data": "synthetic (seeded, shapes and distributions of the configuration)",
         "config": desc,
