@@ -403,6 +403,51 @@ def test_grouped_c4_full_launch_sampled_experts(gpu_lib):
     del w
 
 
+def test_warp_specialized_strided_outputs(gpu_lib):
+    """Outputs whose row stride runs past their columns (ldc > n) on the
+    warp-specialized kernels: the 128x192 forward tiles (two adjacent MFMA
+    tiles stored together, an odd third one alone), the persistent dgrad
+    kernel and the weight gradient with accumulate.  Full outputs against the
+    oracle; the columns between n and ldc keep their sentinel."""
+    rng = np.random.default_rng(231)
+
+    m, n, k = 2113, 2816, 256                      # 198 tiles of 256x128: 128x192 tiles instead
+    qa, qb = random_codes(rng, (m, k)), random_codes(rng, (n, k))
+    sa, sb = random_scales(rng, (m, k // 128)), random_scales(rng, (n // 128, k // 128))
+    big = torch.full((m, n + 64), -1, dtype=torch.int16, device="cuda")
+    gpu_lib.fp8bs_gemm(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), c=big.view(torch.bfloat16)[:, :n])
+    torch.cuda.synchronize()
+    assert bool((big[:, n:] == -1).all())
+    mag = gemm_fprop(magnitude_codes(qa), sa, magnitude_codes(qb), sb)
+    assert_gemm_parity(bf16_values_host(big.view(torch.bfloat16)[:, :n]), gemm_fprop(qa, sa, qb, sb), mag,
+                       label=f"fprop strided {m}x{n}x{k}")
+
+    mo, ko, kc = 2304, 4096, 256                   # dX [mo, ko] = dY [mo, kc] W [kc, ko]: more tiles than CUs
+    qd, sd = random_codes(rng, (mo, kc)), random_scales(rng, (mo, kc // 128))
+    qw, sw = random_codes(rng, (kc, ko)), random_scales(rng, (kc // 128, ko // 128))
+    big = torch.full((mo, ko + 128), -1, dtype=torch.int16, device="cuda")
+    gpu_lib.fp8bs_gemm(to_dev(qd), to_dev(sd), to_dev(qw), to_dev(sw), b_layout=1,
+                       c=big.view(torch.bfloat16)[:, :ko])
+    torch.cuda.synchronize()
+    assert bool((big[:, ko:] == -1).all())
+    mag = gemm_dgrad(magnitude_codes(qd), sd, magnitude_codes(qw), sw)
+    assert_gemm_parity(bf16_values_host(big.view(torch.bfloat16)[:, :ko]), gemm_dgrad(qd, sd, qw, sw), mag,
+                       label=f"dgrad strided {mo}x{ko}x{kc}")
+
+    mw, nw, t = 1536, 4608, 256
+    qa2, qb2 = random_codes(rng, (mw, t)), random_codes(rng, (nw, t))
+    sa2, sb2 = random_scales(rng, (mw, t // 128)), random_scales(rng, (nw, t // 128))
+    args = (to_dev(qa2), to_dev(sa2), to_dev(qb2), to_dev(sb2))
+    big = torch.full((mw, nw + 32), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_lib.fp8bs_gemm_wgrad(*args, c=big[:, :nw])
+    c64 = gemm_wgrad(qa2, sa2, qb2, sb2)
+    mag = gemm_wgrad(magnitude_codes(qa2), sa2, magnitude_codes(qb2), sb2)
+    assert_gemm_parity(big[:, :nw].cpu().numpy(), c64, mag, out_bf16=False, label=f"wgrad strided {mw}x{nw}x{t}")
+    gpu_lib.fp8bs_gemm_wgrad(*args, c=big[:, :nw], accumulate=1)
+    assert_gemm_parity(big[:, :nw].cpu().numpy(), 2 * c64, 2 * mag, out_bf16=False, label="wgrad strided accumulate")
+    assert bool(torch.isnan(big[:, nw:]).all())
+
+
 # --------------------------------------------------------- random shape sweep -----
 
 def _sweep_shapes(seed, count):
