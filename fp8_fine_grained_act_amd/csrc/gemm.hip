@@ -63,6 +63,8 @@ struct GemmArgs {
   int64_t tiles_m, tiles_n;
   int accumulate;
   int64_t group_m;  // band height in m-tiles of the XCD-aware order; 0 = column-major, -1 = row-major
+  float* ws;        // split contraction: FP32 partials [ksplit][m][n] (gridDim.y = ksplit)
+  int64_t ksplit;
 };
 
 // Workgroups are dealt to the chip's 8 XCDs round-robin by workgroup id, and
@@ -543,7 +545,7 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // activation-gradient B slab is stored as copied ([k][n], swz_t layout) and
 // gathered with ds_read_b64_tr_b8 as in gemm_kernel.
 // ---------------------------------------------------------------------------
-template <int MODE, int MW, int BM, int BN, bool PERSIST>
+template <int MODE, int MW, int BM, int BN, bool PERSIST, bool SPLIT = false>
 __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   // MW MFMA waves: 4 (one per SIMD) or 8 (two per SIMD, so one wave's fold
   // VALU work runs under the other's MFMAs; register budget 168 per lane for
@@ -586,13 +588,18 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   // boundaries, so the next tile's first slabs are copied while the MFMA
   // waves store the previous tile.
   const int64_t M = p.m, N = p.n, K = p.k;
-  const int nkb = (int)(K / BK);
+  const int nkb = (int)(K / BK);               // K blocks of a row (the width of the scale rows)
+  // SPLIT: workgroup (x, y) runs slabs [y * nslab, (y + 1) * nslab) of tile x
+  // and stores its FP32 partial to ws[y]; a second kernel sums the partials
+  static_assert(!SPLIT || (MODE == kDgrad && !PERSIST), "split contraction: plain dgrad tiles");
+  const int nslab = SPLIT ? nkb / (int)p.ksplit : nkb;
+  const int kb0 = SPLIT ? (int)blockIdx.y * nslab : 0;
   // PERSIST = false: one tile per workgroup (grid = tiles), with the tile
   // bookkeeping and the store outside the slab loop, which keeps the MFMA
   // waves' registers as in a plain kernel.
   const int64_t G = gridDim.x;
   const int my_tiles = PERSIST ? (int)((p.tiles_m * p.tiles_n - 1 - (int64_t)blockIdx.x) / G + 1) : 1;
-  const int units = my_tiles * nkb;
+  const int units = my_tiles * nslab;
   struct Origin {
     int64_t m0, n0;
   };
@@ -698,11 +705,11 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     int it = 0, ikb = 0;
     set_tile(0);
     auto issue_next = [&](Stage<BM, BN>& s) {
-      if (PERSIST && ikb == nkb) {
+      if (PERSIST && ikb == nslab) {
         ikb = 0;
         set_tile(++it);
       }
-      issue(ikb++, s);
+      issue(kb0 + ikb++, s);
     };
     // prologue: units 0 and 1; unit 0 landed before the first barrier
     issue_next(st0);
@@ -939,7 +946,15 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     for (int j = 0; j < TM; ++j) {
       const int64_t row = m0 + WM * wm + 16 * j + l16;
       if (row >= M) continue;
-      if (MODE != kWgrad) {
+      if (SPLIT) {
+        float* prow = p.ws + ((int64_t)blockIdx.y * M + row) * N;
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const int64_t col = n0 + WN * wn + 16 * i + 4 * g;
+          if (col < N)
+            *reinterpret_cast<float4*>(prow + col) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+      } else if (MODE != kWgrad) {
         store_row_bf16<TN, TM>(p, acc, j, row, n0 + WN * wn, g);
       } else {
 #pragma unroll
@@ -960,7 +975,7 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   };
   int ti = 0, tkb = 0;
   auto after_slab = [&]() {
-    if (!PERSIST || ++tkb < nkb) return;
+    if (!PERSIST || ++tkb < nslab) return;
     fold(TN - 1, TM - 1);
     store_tile();
 #pragma unroll
@@ -1119,6 +1134,71 @@ static bool fits_u32(int64_t bytes) { return bytes < 0xFFFFFFFFLL; }
 #ifndef FP8BS_TILE_SMALL
 #define FP8BS_TILE_SMALL 64, 128, 2, 2, 3
 #endif
+// Split contraction for activation gradients with few output tiles and a long
+// contraction (dX [4096, 512] over 32768: 64 tiles of 256x128 leave three
+// quarters of the CUs idle).  ksplit workgroups per tile each run one
+// contiguous range of K slabs on the warp-specialized kernel and store an
+// FP32 partial; splitk_reduce_kernel sums the partials in split order and
+// rounds once to bf16.  The partials live in a stream-ordered allocation
+// (hipMallocAsync / hipFreeAsync on the call's stream), so calls on different
+// streams never share them.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int64_t ksplit,
+                                                            int64_t m, int64_t n, uint16_t* __restrict__ c,
+                                                            int64_t ldc) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one 4-column group per thread
+  const int64_t qpr = n / 4;
+  if (q >= m * qpr) return;
+  const int64_t row = q / qpr, col = (q - row * qpr) * 4;
+  const int64_t plane = m * n;
+  float4 acc = *reinterpret_cast<const float4*>(ws + row * n + col);
+  for (int64_t k = 1; k < ksplit; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(ws + k * plane + row * n + col);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  uint2 o;
+  o.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+  o.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+  *reinterpret_cast<uint2*>(c + row * ldc + col) = o;
+}
+
+// Contraction split of a dgrad: 1 (none) unless 256x128 tiles would fill at
+// most half the CUs; then the largest power of two that keeps tiles x split
+// within the CUs, divides the K blocks and leaves each split 16 or more.
+static int64_t dgrad_ksplit(int64_t m, int64_t n, int64_t k, int cus) {
+  const int64_t tiles = ((m + 255) / 256) * (n / 128);
+  const int64_t nkb = k / BK;
+  int64_t ks = 1;
+  while (2 * ks * tiles <= cus && nkb % (2 * ks) == 0 && nkb / (2 * ks) >= 16) ks *= 2;
+  return ks;
+}
+
+static int launch_dgrad_split(GemmArgs a, hipStream_t s, int64_t ks) {
+  a.tiles_n = a.n / 128;
+  a.tiles_m = (a.m + 255) / 256;
+  a.group_m = choose_group_m(a, 256, 128, 2);
+  a.ksplit = ks;
+  const int64_t tiles = a.tiles_m * a.tiles_n;
+  const int64_t groups = a.m * a.n / 4;
+  if (tiles > kMaxGrid || ks > 65535 || (groups + 255) / 256 > kMaxGrid) return FP8BS_ERR_SHAPE;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, (size_t)ks * (size_t)a.m * (size_t)a.n * sizeof(float), s) != hipSuccess)
+    return FP8BS_ERR_LAUNCH;
+  a.ws = static_cast<float*>(ws);
+  hipLaunchKernelGGL((gemm_ws_kernel<kDgrad, 8, 256, 128, false, true>), dim3((unsigned)tiles, (unsigned)ks),
+                     dim3(64 * 12), 0, s, a);
+  int st = launch_status();
+  if (st == FP8BS_OK) {
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, a.ws, ks,
+                       a.m, a.n, static_cast<uint16_t*>(a.c), a.ldc);
+    st = launch_status();
+  }
+  if (hipFreeAsync(ws, s) != hipSuccess && st == FP8BS_OK) st = FP8BS_ERR_LAUNCH;
+  return st;
+}
+
 static bool small_tiles(int64_t m, int64_t n) {
   return ((m + 127) / 128) * ((n + 127) / 128) < cu_count();
 }
@@ -1133,7 +1213,11 @@ extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb,
   if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
       ldc % 8)
     return FP8BS_ERR_ALIGN;
-  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, k, nullptr, 0, 0, 0, 0, 0};
+  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, k, nullptr, 0, 0, 0, 0, 0, nullptr, 1};
+  if (b_layout == 1) {
+    const int64_t ks = dgrad_ksplit(m, n, k, cu_count());
+    if (ks > 1) return launch_dgrad_split(a, (hipStream_t)stream, ks);
+  }
   if (use_ws(m, n)) {
     if (b_layout == 0) return launch_gemm_ws<kFprop>(a, (hipStream_t)stream, cu_count());
     return launch_gemm_ws<kDgrad>(a, (hipStream_t)stream, cu_count());

@@ -147,6 +147,15 @@ int fp8bs_quantize_w_128x128(const uint16_t* w, int64_t n, int64_t k, int64_t ld
  *   c   bf16 [m, n], row stride ldc elements
  *   m >= 1 (any), n % 128 == 0, k % 128 == 0.
  * Alignment: qa, qb, c 16-byte aligned; ldc % 8 == 0, ldc >= n.
+ * Workspace (b_layout == 1 only): when the output's 256x128 tiles would fill
+ * at most half the compute units and the contraction is long (at least 32
+ * blocks), the contraction is split over workgroups.  Their FP32 partials,
+ * split x m x n x 4 bytes (split <= the compute-unit count / tiles), take a
+ * stream-ordered allocation on `stream` (hipMallocAsync, freed with
+ * hipFreeAsync after the summing kernel).  Graph capture records both.  The
+ * partials are summed in split order and rounded once, so the result is
+ * deterministic but not bit-identical to an unsplit run.  FP8BS_ERR_LAUNCH if
+ * the allocation fails.
  */
 int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
                int64_t m, int64_t n, int64_t k, int b_layout, uint16_t* c, int64_t ldc,

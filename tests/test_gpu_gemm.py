@@ -448,6 +448,27 @@ def test_warp_specialized_strided_outputs(gpu_lib):
     assert bool(torch.isnan(big[:, nw:]).all())
 
 
+def test_dgrad_split_contraction(gpu_lib):
+    """Activation gradients whose 256x128 tiles fill at most half the CUs and
+    whose contraction is long split the contraction over workgroups (FP32
+    partials summed in split order, one rounding to bf16): ragged M, splits of
+    4 and 2, a strided output whose padding columns keep their sentinel."""
+    rng = np.random.default_rng(241)
+    for mo, ko, kc in [(1000, 256, 8192), (300, 512, 4096), (4096, 512, 32768)]:
+        qd, sd = random_codes(rng, (mo, kc)), random_scales(rng, (mo, kc // 128))
+        qw, sw = random_codes(rng, (kc, ko)), random_scales(rng, (kc // 128, ko // 128))
+        big = torch.full((mo, ko + 64), -1, dtype=torch.int16, device="cuda")
+        gpu_lib.fp8bs_gemm(to_dev(qd), to_dev(sd), to_dev(qw), to_dev(sw), b_layout=1,
+                           c=big.view(torch.bfloat16)[:, :ko])
+        torch.cuda.synchronize()
+        assert bool((big[:, ko:] == -1).all())
+        got = bf16_values_host(big.view(torch.bfloat16)[:, :ko])
+        rows = _sample_rows(mo, 96, seed=kc) if mo * kc > 2 ** 26 else np.arange(mo)
+        mag = gemm_dgrad(magnitude_codes(qd[rows]), sd[rows], magnitude_codes(qw), sw)
+        assert_gemm_parity(got[rows], gemm_dgrad(qd[rows], sd[rows], qw, sw), mag,
+                           label=f"dgrad split {mo}x{ko}x{kc}")
+
+
 # --------------------------------------------------------- random shape sweep -----
 
 def _sweep_shapes(seed, count):

@@ -1,8 +1,9 @@
 """HIP-graph capture of a whole training pass of a linear layer.
 
 The library's calls are plain kernel launches on the caller's stream (no
-allocation, no memset, no host synchronisation), so a captured pass must
-replay to exactly the eager result.  The graph is replayed several times with
+memset, no host synchronisation; the one allocation, the split-contraction
+dgrad's workspace, is stream-ordered and recorded by the capture), so a
+captured pass must replay to exactly the eager result.  The graph is replayed several times with
 unrelated eager work and synchronisations between the replays; every replay
 is compared bit for bit with the eager launches, and the eager result itself
 is checked against the oracle.
@@ -140,3 +141,35 @@ def test_moe_forward_graph_replays_match_eager(gpu_lib):
         torch.cuda.synchronize()
         for i, (t, rb) in enumerate(zip(outs, ref)):
             assert torch.equal(_bits(t), rb), f"replay {rep}: MoE output {i} differs from the eager pass"
+
+
+def test_split_contraction_dgrad_graph_replays_match_eager(gpu_lib):
+    """The split-contraction dgrad (few output tiles, long contraction) takes its
+    FP32 partials from a stream-ordered allocation; captured in a graph, its
+    replays reproduce the eager bits."""
+    rng = np.random.default_rng(251)
+    mo, ko, kc = 300, 512, 4096
+    qd = torch.from_numpy(rng.integers(0, 0x7E, (mo, kc), dtype=np.uint8)).cuda()
+    sd = torch.from_numpy(rng.uniform(0.5, 2.0, (mo, kc // 128)).astype(np.float32)).cuda()
+    qw = torch.from_numpy(rng.integers(0, 0x7E, (kc, ko), dtype=np.uint8)).cuda()
+    sw = torch.from_numpy(rng.uniform(0.5, 2.0, (kc // 128, ko // 128)).astype(np.float32)).cuda()
+    out = torch.empty((mo, ko), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.fp8bs_gemm(qd, sd, qw, sw, b_layout=1, c=out)
+    torch.cuda.synchronize()
+    ref = _bits(out).clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            gpu_lib.fp8bs_gemm(qd, sd, qw, sw, b_layout=1, c=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.view(torch.int16).fill_(-1)
+        gpu_lib.fp8bs_gemm(qd, sd, qw, sw, b_layout=1)      # unrelated eager work of the same kind
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), ref), f"replay {rep} differs from the eager result"
