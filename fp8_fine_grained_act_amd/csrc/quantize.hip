@@ -90,10 +90,10 @@ __device__ __forceinline__ int qswz(int row) { return (row & 15) ^ (((row >> 5) 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 // STREAM: the input is larger than half the last-level cache, so it is read
-// with the non-temporal hint (cold 16384 x 7168: 78 -> 72 us); an input that fits
-// may still be cached from its producer, and the hint loses those hits
-// (warm 16384 x 1536: 14.7 -> 18.5 us).  The fused kernel is slower with the
-// hint in both cases and never streams.
+// with the non-temporal hint (cold 16384 x 7168: 78 -> 72 us; the fused
+// kernel on 4096 x 32768: 125 -> 112 us); an input that fits may still be
+// cached from its producer, and the hint loses those hits (warm 16384 x 1536:
+// 14.7 -> 18.5 us; the fused kernel on inputs that fit is slower with it too).
 template <bool ROWS, bool STREAM = false>
 __global__ __launch_bounds__(256) void quant_act_cols_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t rows, int64_t cols,
@@ -312,8 +312,12 @@ extern "C" int fp8bs_quantize_act_1x128_dual(const uint16_t* x, int64_t rows, in
       !aligned(scales_t, 4) || ldx % 8 || ldq % 16 || ldqt % 16)
     return FP8BS_ERR_ALIGN;
   if (!cols_grid_ok(rows, cols)) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_act_cols_kernel<true>, cols_grid(rows, cols), dim3(256), 0,
-                     (hipStream_t)stream, x, ldx, rows, cols, qt, ldqt, scales_t, q, ldq, scales);
+  if (rows * cols * 2 > kStreamBytes)
+    hipLaunchKernelGGL((quant_act_cols_kernel<true, true>), cols_grid(rows, cols), dim3(256), 0,
+                       (hipStream_t)stream, x, ldx, rows, cols, qt, ldqt, scales_t, q, ldq, scales);
+  else
+    hipLaunchKernelGGL(quant_act_cols_kernel<true>, cols_grid(rows, cols), dim3(256), 0,
+                       (hipStream_t)stream, x, ldx, rows, cols, qt, ldqt, scales_t, q, ldq, scales);
   return launch_status();
 }
 
