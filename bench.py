@@ -1,26 +1,38 @@
 #!/usr/bin/env python3
 """Benchmark of the block-scaled FP8 GEMM path on one MI355X.
 
-Default workload (one "step" = one FP8 training pass of the MLA query
-down-projection layer, X [4096, 7168] -> Y [4096, 1536], all quantization
-included; this runs every step of the hot path except the MoE grouped GEMM):
-    quantize X (1x128 tiles)             quantize W (128x128 blocks)
-    Y  = X W^T   (forward GEMM, bf16)    quantize dY (1x128 tiles)
-    dX = dY W    (dgrad GEMM, bf16)      quantize dY^T, X^T (tiles along tokens)
-    dW = dY^T X  (wgrad GEMM, f32)
-``value`` = the step's GEMM FLOPs (3 x 2*4096*1536*7168) / step time, in TFLOP/s.
-Other configurations (``--config c3|c4|c5``) print their own line.
+Default workload (``--config c4``, the largest configuration): the MoE routed-
+expert grouped GEMM of 4096 tokens x top-8 of 256 experts (Zipf 1.1 counts,
+each expert's rows padded to a multiple of 128), fused gate+up N = 4096,
+K = 7168.  One step runs the configuration's whole FP8 path:
+    quantize X (1x128 tiles, the padded expert-major rows)
+    quantize every expert's W (128x128 blocks, 256 x 4096 x 7168)
+    grouped GEMM C = X W_e^T per expert segment (bf16 out)
+``value`` = the grouped GEMM's FLOPs over the routed (real) rows,
+2 * 32768 * 4096 * 7168, divided by the step time, in TFLOP/s.  The MoE
+routing, dispatch (permute + quantize from token order) and combine around it
+are timed on their own and reported under ``moe_kernels`` (not in ``value``).
 
-Inputs are resident in HBM before timing; the step rotates over several input
-copies (>= 512 MB in total) so the 256 MB Infinity Cache cannot hold them
-between steps.  The timed steps are eager launches on one stream: the host
-enqueues ahead of the GPU (its wall time per step matches the GPU's), and on
-ROCm a HIP graph replay per step measured ~30 us slower than the same launches
-made eagerly.  ``--graph`` times one captured graph per step instead (each
+Other configurations print their own line: ``--config c2|c3`` one FP8
+training pass of a linear layer (quantize X, W, dY; forward, dgrad and wgrad
+GEMMs), ``--config c5`` the weight gradient over 16384 tokens (both operands
+transpose-quantized).
+
+Inputs are resident in HBM before timing; small configurations rotate over
+several input copies (>= 512 MB in total) so the 256 MB Infinity Cache cannot
+hold them between steps (c4's 15 GB of expert weights need no rotation).  The
+timed steps are eager launches on one stream, bracketed by device
+synchronizations; ``--graph`` times one captured graph per step instead (each
 replay is first checked bit for bit against the eager launches).  Per-kernel
-durations come from a second timed region on the same stream: every call is
-captured ``--kernel-reps`` times in a row into a graph of its own (rotating
-over the input copies) and timed with HIP events around the replay.
+durations come from a second timed region: each call is captured
+``--kernel-reps`` times in a row into a graph of its own (rotating over the
+input copies) and timed with HIP events on the stream it is launched on.
+
+Each call carries its own roofline bound: the larger of its FLOPs at the FP8
+dense peak (5 PFLOP/s) and its algorithmic bytes at the HBM peak (8 TB/s).
+``roofline`` is the call with the largest time, ``roofline_gemm`` the GEMM of
+the step with the largest time.  ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload on the host cores.
 """
 
 import argparse
@@ -55,13 +67,17 @@ def parse_args():
     # the GPU reaches its steady clock only after ~10 ms of back-to-back work
     # (c2 steps measured 245 -> 223 -> 217 us over three runs of 50): the
     # default warm-up covers that, and the timed steps last ~50 ms
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=50)
-    p.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"])
+    # (c4's step lasts ~6 ms, so any warm-up settles it; the layer
+    # configurations take the longer defaults below when none is given)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--config", default="c4", choices=["c2", "c3", "c4", "c5"])
     p.add_argument("--rotate", type=int, default=0, help="input copies to rotate over (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=4096)
-    p.add_argument("--kernel-reps", type=int, default=24, help="launches per per-kernel timing graph")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="the CPU oracle repeats its sample until this much host time has passed")
+    p.add_argument("--kernel-reps", type=int, default=None,
+                   help="launches per per-kernel timing graph (default 24; 6 for c4)")
     p.add_argument("--graph", action="store_true",
                    help="time one HIP graph replay per step instead of eager launches")
     p.add_argument("--eager", action="store_true", help="eager launches (the default; kept for old command lines)")
@@ -72,7 +88,15 @@ def parse_args():
                         "weight gradient's tiles along the tokens are re-tiled from them")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 512 MiB device-to-device copies (reference for HBM byte counters)")
-    return p.parse_args()
+    a = p.parse_args()
+    small = a.config != "c4"
+    if a.steps is None:
+        a.steps = 200 if small else 20
+    if a.warmup is None:
+        a.warmup = 50 if small else 5
+    if a.kernel_reps is None:
+        a.kernel_reps = 24 if small else 6
+    return a
 
 
 def source_hash(kind):
@@ -203,80 +227,87 @@ def build_layer_step(lib, cfg_name, rotate, dual=True, act_cache=False):
                                          "re-tiled from it; dY: one call for both orientations") if act_cache
                 else "one call per tensor for both orientations" if dual
                 else "one call per tensor and orientation")
-    return calls, state, desc, d
+    return calls, state, desc, dict(d, kind="layer", cfg=cfg), []
 
 
 def build_grouped_step(lib, rotate):
-    """Calls of the MoE routed-expert forward around the grouped GEMM (config c4 shapes).
+    """Calls of configuration c4: the MoE expert grouped GEMM with its quantization.
 
-    route (expert-major padded layout from the top-k ids) -> dispatch payload
-    (token rows coded once in 1x128 tiles, stored to their k rows) -> quantize
-    every expert's weight -> grouped GEMM over the row capacity -> combine
-    (gate-weighted sum of each token's k expert-output rows, bf16).  The
-    combine's expert outputs are [capacity, 7168] bf16 (the model width, the
-    shape the down projection returns); they are drawn once on the device.
-    No call reads a size back to the host.
+    The step: quantize X (1x128 tiles over the padded expert-major rows; the
+    padding rows are +0.0) -> quantize every expert's weight (128x128 blocks)
+    -> grouped GEMM over the padded total.  The MoE routing layout, the
+    dispatch payload (permute + 1x128 quantize from token order) and the
+    combine (gate-weighted sum of each token's k expert rows, [capacity, 7168]
+    bf16 expert outputs drawn once on the device) are returned as extra calls:
+    they are timed on their own, outside the step.  No call reads a size back
+    to the host.
     """
     import numpy as np
     import torch
 
-    from workloads import config_by_name, device_expert_weights, moe_dispatch_inputs, moe_routing
+    from workloads import (config_by_name, device_expert_weights, grouped_inputs_host, moe_dispatch_inputs)
 
     cfg = config_by_name("c4")
-    d = moe_dispatch_inputs(cfg)
-    route = moe_routing(cfg)
-    counts, total = route["counts"], int(route["offsets"][-1])
-    tokens, topk = d["ids"].shape
+    host = grouped_inputs_host(cfg, with_weights=False)
+    counts, offsets = host["counts"], host["offsets"]
+    total = int(offsets[-1])
     k, n, num_e = cfg["K"], cfg["N"], cfg["experts"]
-    cap = lib.fp8bs_moe_max_rows(tokens, topk, num_e)
-    x = dev_bf16(d["x"])
-    ids = torch.from_numpy(d["ids"]).cuda()
-    gates = torch.from_numpy(d["gates"]).cuda()
+    pairs = int(counts.sum())
+    x = dev_bf16(host["x"])
+    seg_pad = torch.from_numpy(offsets.astype(np.int32)).cuda()
     w = device_expert_weights(cfg)
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(4004)
-    y_down = torch.randn((cap, k), generator=gen, device="cuda").to(torch.bfloat16)
     i32, u8, f32, bf16 = torch.int32, torch.uint8, torch.float32, torch.bfloat16
     e = lambda *s, dt: torch.empty(s, dtype=dt, device="cuda")  # noqa: E731
-    seg, slot, tok = e(num_e + 1, dt=i32), e(tokens, topk, dt=i32), e(cap, dt=i32)
-    qx, sx = e(cap, k, dt=u8), e(cap, k // 128, dt=f32)
+    qx, sx = e(total, k, dt=u8), e(total, k // 128, dt=f32)
     qw, sw = e(num_e, n, k, dt=u8), e(num_e, n // 128, k // 128, dt=f32)
-    y = e(cap, n, dt=bf16)
-    out = e(tokens, k, dt=bf16)
+    y = e(total, n, dt=bf16)
     state = {"i": 0}
-    pairs = int(counts.sum())
-    seg_rows = np.diff(route["offsets"])
-    scanned = int(np.minimum(seg_rows, 128).sum())          # row tokens read by the padding workgroups
+    kb = k // 128
+    # algorithmic bytes over the padded rows (the rows the kernels read and write)
+    x_bytes = total * k * 3 + total * kb * 4
+    w_bytes = num_e * n * k * 3 + num_e * (n // 128) * kb * 4
+    gemm_bytes = total * (k + kb * 4) + num_e * (n * k + (n // 128) * kb * 4) + total * n * 2
     calls = [
+        Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, q=qx, scales=sx),
+             nbytes=x_bytes, outs=(qx, sx)),
+        Call("quant_w_experts", "quant", lambda: lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw),
+             nbytes=w_bytes, outs=(qw, sw)),
+        Call("gemm_grouped", "gemm", lambda: lib.fp8bs_grouped_gemm(qx, sx, seg_pad, qw, sw, c=y),
+             flops=2.0 * pairs * n * k, nbytes=gemm_bytes, outs=(y,)),
+    ]
+
+    # the MoE kernels around the grouped GEMM (timed on their own)
+    d = moe_dispatch_inputs(cfg)
+    tokens, topk = d["ids"].shape
+    cap = lib.fp8bs_moe_max_rows(tokens, topk, num_e)
+    xt = dev_bf16(d["x"])
+    ids = torch.from_numpy(d["ids"]).cuda()
+    gates = torch.from_numpy(d["gates"]).cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4004)
+    y_down = torch.randn((cap, k), generator=gen, device="cuda").to(bf16)
+    seg, slot, tok = e(num_e + 1, dt=i32), e(tokens, topk, dt=i32), e(cap, dt=i32)
+    dq, ds = e(cap, k, dt=u8), e(cap, kb, dt=f32)
+    out = e(tokens, k, dt=bf16)
+    seg_rows = np.diff(offsets)
+    scanned = int(np.minimum(seg_rows, 128).sum())          # row tokens read by the padding workgroups
+    extras = [
         Call("moe_route", "moe", lambda: lib.fp8bs_moe_route(ids, num_e, rows_cap=cap, seg_offsets=seg,
                                                                 slot_rows=slot, row_token=tok),
              nbytes=tokens * topk * 4 * 2 + cap * 4 + (num_e + 1) * 4, outs=(seg, slot, tok)),
-        Call("moe_dispatch_x", "moe", lambda: lib.fp8bs_moe_permute_quantize(x, slot, seg, tok, q=qx, scales=sx),
-             nbytes=tokens * k * 2 + tokens * topk * 4 + scanned * 4 + total * (k + k // 128 * 4),
-             outs=(qx, sx)),
-        Call("quant_w_experts", "quant", lambda: lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw),
-             nbytes=num_e * n * k * 3 + num_e * (n // 128) * (k // 128) * 4, outs=(qw, sw)),
-        Call("gemm_grouped", "gemm", lambda: lib.fp8bs_grouped_gemm(qx, sx, seg, qw, sw, c=y),
-             flops=2.0 * pairs * n * k,
-             nbytes=pairs * (k + k // 128 * 4) + num_e * (n * k + (n // 128) * (k // 128) * 4) + pairs * n * 2,
-             outs=(y,)),
+        Call("moe_dispatch_x", "moe", lambda: lib.fp8bs_moe_permute_quantize(xt, slot, seg, tok, q=dq, scales=ds),
+             nbytes=tokens * k * 2 + tokens * topk * 4 + scanned * 4 + total * (k + kb * 4), outs=(dq, ds)),
         Call("moe_combine", "moe", lambda: lib.fp8bs_moe_combine(y_down, slot, gates, out=out),
              nbytes=pairs * k * 2 + tokens * topk * 8 + tokens * k * 2, outs=(out,)),
     ]
-    # rows past the padded total are never written; the replay check compares
-    # only what the step defines
-    for c in calls:
-        if c.name == "moe_dispatch_x":
-            c.outs = [qx[:total], sx[:total]]
-        elif c.name == "gemm_grouped":
-            c.outs = [y[:total]]
-    desc = dict(workload="c4: MoE routed-expert forward, 4096 tokens x top-8 of 256 experts (Zipf 1.1), "
-                         "fused gate+up N=4096, K=7168: route, dispatch (permute + 1x128 quantize), quantize all "
-                         "expert weights, grouped GEMM over the row capacity, combine of [capacity, 7168] bf16 "
-                         "expert outputs",
-                routed_rows=pairs, padded_rows=total, row_capacity=cap, experts=num_e, N=n, K=k,
-                gemm_flops_counted="real routed rows only")
-    return calls, state, desc, None
+    desc = dict(workload="c4: MoE expert grouped GEMM, 4096 tokens x top-8 of 256 experts (Zipf 1.1 counts, "
+                         "rows padded to 128 per expert), fused gate+up N=4096, K=7168; step = 1x128 quantization "
+                         "of the padded rows + 128x128 quantization of all 256 expert weights + grouped GEMM",
+                routed_rows=pairs, padded_rows=total, experts=num_e, N=n, K=k,
+                value_flops="grouped GEMM over the routed rows, 2*32768*4096*7168",
+                bytes_counted="padded rows")
+    data = dict(kind="c4", x=host["x"], counts=counts, offsets=offsets, w_dev=w, cfg=cfg)
+    return calls, state, desc, data, extras
 
 
 def build_wgrad_step(lib, rotate, act_cache=False):
@@ -315,7 +346,7 @@ def build_wgrad_step(lib, rotate, act_cache=False):
     desc = dict(workload="c5: weight gradient dW[1536,7168] = dY^T X over 16384 tokens, " + (
                     "dY transpose-quantized along tokens, X re-tiled along tokens from its cached FP8 forward tiles"
                     if act_cache else "both operands transpose-quantized along tokens"), T=t, M=m, N=n)
-    return calls, state, desc, None
+    return calls, state, desc, dict(d, kind="wgrad", cfg=cfg), []
 
 
 def run_steps(calls, state, steps):
@@ -432,26 +463,40 @@ def copy_rate_gbps(reps=8):
     return rate
 
 
-def cpu_baseline(cfg_name, data, sample_rows, min_seconds=10.0):
-    """The oracle, as it stands, on a bounded sample of the same workload (host cores).
+def host_threads():
+    """Host threads the CPU oracle runs its matrix products on: the affinity
+    mask, capped by OMP_NUM_THREADS where the environment sets it."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
 
-    The sample is the training pass over the first ``sample_rows`` tokens (the
-    whole weight is quantized every pass), repeated until ``min_seconds`` of
-    host time have passed; value = sampled GEMM FLOPs / mean pass time.
-    """
+
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = 1
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def _oracle_sample_layer(data):
+    """c2 / c3: the whole training pass over the first tokens (the full weight quantized each pass)."""
     from oracle import (gemm_dgrad, gemm_fprop, gemm_wgrad, quantize_act_1x128, quantize_act_1x128_t,
                         quantize_w_128x128)
 
-    x, w, dy = data["a"][:sample_rows], data["b"], data["dy"][:sample_rows]
+    rows = 4096 if data["cfg"]["name"] == "c2" else 1024
+    x, w, dy = data["a"][:rows], data["b"], data["dy"][:rows]
     m, k = x.shape
     n = w.shape[0]
-    passes, t0 = 0, time.perf_counter()
-    while True:
+
+    def one():
         qx, sx = quantize_act_1x128(x)
         qw, sw = quantize_w_128x128(w)
         gemm_fprop(qx, sx, qw, sw)
@@ -460,17 +505,129 @@ def cpu_baseline(cfg_name, data, sample_rows, min_seconds=10.0):
         qdyt, sdyt = quantize_act_1x128_t(dy)
         qxt, sxt = quantize_act_1x128_t(x)
         gemm_wgrad(qdyt, sdyt, qxt, sxt)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    per_pass = dt / passes
-    flops = 3 * 2.0 * m * n * k
-    return {"value": flops / per_pass / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3), "passes": passes,
-            "sample": f"{cfg_name} training pass over {m} of {data['a'].shape[0]} tokens (whole weight "
-                      f"[{n},{k}] quantized each pass; forward, dgrad and wgrad GEMMs), repeated {passes}x; "
-                      f"value = GEMM FLOPs per pass / mean pass wall time"}
+
+    text = (f"training pass over {m} of {data['a'].shape[0]} tokens: quantize X, dY (both orientations) and the "
+            f"whole weight [{n},{k}], forward, dgrad and wgrad GEMMs; value = GEMM FLOPs / pass wall time")
+    return one, 3 * 2.0 * m * n * k, text
+
+
+def _oracle_sample_grouped(data, rows=512):
+    """c4: the step's costs measured on a sample and scaled to the whole step.
+
+    Every expert's weight has the same shape, so one expert's 128x128
+    quantization stands for each of the 256; the 1x128 quantization and the
+    GEMM cost in proportion to their rows, so ``rows`` routed rows of the
+    largest expert (a GEMM of realistic height) stand for the padded rows
+    (quantization) and the routed rows (GEMM).  Returns the sample and a
+    function that turns the sample's time into the whole step's time.
+    """
+    import numpy as np
+    import torch
+
+    from oracle import gemm_fprop, quantize_act_1x128, quantize_w_128x128
+
+    counts, off, x = data["counts"], data["offsets"], data["x"]
+    n, k = data["cfg"]["N"], data["cfg"]["K"]
+    num_e, routed, padded = len(counts), int(counts.sum()), int(off[-1])
+    e0 = int(np.argmax(counts))
+    rows = min(rows, int(counts[e0]))
+    xs = x[off[e0]:off[e0] + rows]
+    # the weights were drawn on the device (seeded torch generator); their bf16 bits come back unchanged
+    w0 = data["w_dev"][e0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    parts = {"w": 0.0, "x": 0.0, "gemm": 0.0}
+
+    def one():
+        t0 = time.perf_counter()
+        qw, sw = quantize_w_128x128(w0)
+        t1 = time.perf_counter()
+        qx, sx = quantize_act_1x128(xs)
+        t2 = time.perf_counter()
+        gemm_fprop(qx, sx, qw, sw)
+        t3 = time.perf_counter()
+        parts["w"] += t1 - t0
+        parts["x"] += t2 - t1
+        parts["gemm"] += t3 - t2
+
+    def step_seconds(reps):
+        return (num_e * parts["w"] + padded / rows * parts["x"] + routed / rows * parts["gemm"]) / reps
+
+    text = (f"128x128 quantization of expert #{e0}'s weight [{n},{k}] (x{num_e} experts), 1x128 quantization of "
+            f"{rows} of its routed rows (x{padded / rows:.1f} for the {padded} padded rows) and their GEMM "
+            f"(x{routed / rows:.1f} for the {routed} routed rows); value = the step's routed-row GEMM FLOPs / "
+            f"the step time so scaled")
+    return one, 2.0 * routed * n * k, text, step_seconds
+
+
+def _oracle_sample_wgrad(data, tokens=2048):
+    """c5: the weight gradient over the first tokens (both operands transpose-quantized)."""
+    from oracle import gemm_wgrad, quantize_act_1x128_t
+
+    dy, x = data["dy"][:tokens], data["x"][:tokens]
+    m, n = dy.shape[1], x.shape[1]
+
+    def one():
+        qa, sa = quantize_act_1x128_t(dy)
+        qb, sb = quantize_act_1x128_t(x)
+        gemm_wgrad(qa, sa, qb, sb)
+
+    text = (f"weight gradient [{m},{n}] over the first {tokens} of {data['dy'].shape[0]} tokens: both operands "
+            f"transpose-quantized, then the GEMM; value = GEMM FLOPs / wall time")
+    return one, 2.0 * m * n * tokens, text
+
+
+def cpu_baseline(data, min_seconds=10.0):
+    """The oracle, as it stands, on a bounded sample of the configuration (host cores).
+
+    The sample is repeated until ``min_seconds`` of host time have passed;
+    value = the sample's GEMM FLOPs / mean wall time per repetition, in TFLOP/s.
+    numpy's matrix products run on ``cores`` BLAS threads; its elementwise
+    steps (decode, quantization) on one.
+    """
+    threads = host_threads()
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=threads, user_api="blas")
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        limit = None
+    try:
+        kind = data["kind"]
+        scale = None
+        if kind == "c4":
+            one, flops, text, scale = _oracle_sample_grouped(data)
+        else:
+            one, flops, text = _oracle_sample_layer(data) if kind == "layer" else _oracle_sample_wgrad(data)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            one()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    per_rep = scale(reps) if scale else dt / reps
+    return {"value": round(flops / per_rep / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(), "seconds": round(dt, 3), "repetitions": reps,
+            "sample": f"{data['cfg']['name']}: {text}; repeated {reps}x"}
+
+
+def call_roofline(c, avg_s):
+    """The bound of one call and how close its average duration comes to it.
+
+    The bound is whichever takes longer at the MI355X peaks: the call's FLOPs
+    at the dense FP8 MFMA rate, or its algorithmic bytes at the HBM rate.
+    ``achieved`` is the same quantity (FLOPs or bytes) per second.
+    """
+    t_mfma = c.flops / (FP8_PEAK_TFLOPS * 1e12)
+    t_hbm = c.nbytes / (HBM_PEAK_GBPS * 1e9)
+    if c.flops > 0 and t_mfma >= t_hbm:
+        ach = c.flops / avg_s / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / FP8_PEAK_TFLOPS, 4), "algorithmic": c.flops}
+    ach = c.nbytes / avg_s / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBPS, 4), "algorithmic": c.nbytes}
 
 
 def load_traffic(name, kind):
@@ -509,12 +666,12 @@ def main():
         return
 
     if args.config in ("c2", "c3"):
-        calls, state, desc, data = build_layer_step(lib, args.config, args.rotate, dual=not args.separate_quant,
-                                                    act_cache=args.act_cache)
+        calls, state, desc, data, extras = build_layer_step(lib, args.config, args.rotate,
+                                                            dual=not args.separate_quant, act_cache=args.act_cache)
     elif args.config == "c4":
-        calls, state, desc, data = build_grouped_step(lib, args.rotate)
+        calls, state, desc, data, extras = build_grouped_step(lib, args.rotate)
     else:
-        calls, state, desc, data = build_wgrad_step(lib, args.rotate, act_cache=args.act_cache)
+        calls, state, desc, data, extras = build_wgrad_step(lib, args.rotate, act_cache=args.act_cache)
     if args.act_cache:
         data = None                      # the CPU baseline times the plain pass only
     torch.cuda.synchronize()
@@ -547,7 +704,7 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     # the step's own roofline: per call, its FLOPs at the FP8 peak or its
-    # compulsory bytes at the HBM peak, whichever takes longer
+    # algorithmic bytes at the HBM peak, whichever takes longer
     roof_step_us = sum(max(c.flops / (FP8_PEAK_TFLOPS * 1e12), c.nbytes / (HBM_PEAK_GBPS * 1e9))
                        for c in calls) * 1e6
     gemm_flops = sum(c.flops for c in calls)
@@ -555,43 +712,37 @@ def main():
 
     # per-kernel durations (second timed region, same stream discipline);
     # --kernel-reps 0 skips it (profiler runs), leaving the step average per call
+    timed = calls + extras
     if args.kernel_reps > 0:
-        for c, ms in zip(calls, time_kernels(calls, state, rotate, args.kernel_reps)):
+        for c, ms in zip(timed, time_kernels(timed, state, rotate, args.kernel_reps)):
             c.times_ms.append(ms)
     else:
         for c in calls:
             c.times_ms.append(ms_per_step / len(calls))
+        extras = []
     kernel_sum_us = sum(c.times_ms[0] for c in calls) * 1e3
     copy_gbps = copy_rate_gbps() if args.kernel_reps > 0 else None
 
-    kernels = {}
-    for c in calls:
-        avg = sum(c.times_ms) / len(c.times_ms)
-        ent = {"avg_us": round(avg * 1e3, 2)}
+    def entry(c):
+        avg_s = sum(c.times_ms) / len(c.times_ms) * 1e-3
+        ent = {"avg_us": round(avg_s * 1e6, 2)}
+        ent.update(call_roofline(c, avg_s))
         if c.kind == "gemm":
-            tf = c.flops / (avg * 1e-3) / 1e12
-            ent.update(tflops=round(tf, 1), frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4))
-        else:
-            gb = c.nbytes / (avg * 1e-3) / 1e9
-            ent.update(gbps=round(gb, 1), frac_hbm_peak=round(gb / HBM_PEAK_GBPS, 4))
-            if copy_gbps:
-                ent["frac_copy"] = round(gb / copy_gbps, 4)
-        tr = load_traffic(f"{args.config}:{c.name}", c.kind)
-        if tr is not None:
-            ent["traffic"] = tr
-        kernels[c.name] = ent
+            ent["frac_fp8_peak"] = round(c.flops / avg_s / 1e12 / FP8_PEAK_TFLOPS, 4)
+        elif copy_gbps:
+            ent["frac_copy"] = round(c.nbytes / avg_s / 1e9 / copy_gbps, 4)
+        ent["traffic"] = load_traffic(f"{args.config}:{c.name}", c.kind)
+        return ent
+
+    kernels = {c.name: entry(c) for c in calls}
     dom = max(calls, key=lambda c: sum(c.times_ms))
-    avg = sum(dom.times_ms) / len(dom.times_ms) * 1e-3
-    if dom.kind == "gemm":
-        ach = dom.flops / avg / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / FP8_PEAK_TFLOPS, 4)}
-    else:
-        ach = dom.nbytes / avg / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4)}
-    roof["kernel"] = dom.name
-    roof["traffic"] = load_traffic(f"{args.config}:{dom.name}", dom.kind)
+    roof = dict(kernels[dom.name], kernel=dom.name)
+    roof.pop("avg_us", None)
+    gemms = [c for c in calls if c.kind == "gemm"]
+    roof_gemm = None
+    if gemms:
+        g = max(gemms, key=lambda c: sum(c.times_ms))
+        roof_gemm = dict(kernels[g.name], kernel=g.name)
 
     out = {
         "metric": METRIC,
@@ -606,19 +757,22 @@ def main():
         "vs_baseline": None,
         "pct_of_fp8_dense_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "step_roofline": {"us": round(roof_step_us, 1), "pct": round(100 * roof_step_us / (ms_per_step * 1e3), 1),
-                          "note": "per call max(FLOPs / 5 PFLOP/s, compulsory bytes / 8 TB/s), summed"},
+                          "note": "per call max(FLOPs / 5 PFLOP/s, algorithmic bytes / 8 TB/s), summed"},
         "dtype": "fp8_e4m3 (fp32 accumulate)",
         "data": "synthetic (seeded, shapes and distributions of the configuration)",
         "config": desc,
         "roofline": roof,
+        "roofline_gemm": roof_gemm,
         "kernels": kernels,
         "timing": {"step": "eager launches on one stream" if graphs is None else "one HIP graph per step "
                    "(replay checked bit-identical to eager launches)", "kernel_sum_us": round(kernel_sum_us, 1),
-                   "kernel_reps": args.kernel_reps},
+                   "kernel_reps": args.kernel_reps, "warmup_steps_untimed": args.warmup},
         "hbm_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
     }
+    if extras:
+        out["moe_kernels"] = {c.name: entry(c) for c in extras}
     if not args.no_cpu_baseline and data is not None:
-        out["cpu_baseline"] = cpu_baseline(args.config, data, args.cpu_sample_rows)
+        out["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

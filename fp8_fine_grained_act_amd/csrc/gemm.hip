@@ -1129,32 +1129,21 @@ static bool use_ws(int64_t m, int64_t n) {
 // A or B, and the dgrad weight as a whole, must stay below 4 GiB.
 static bool fits_u32(int64_t bytes) { return bytes < 0xFFFFFFFFLL; }
 
-#ifndef FP8BS_TILE_FPROP
-#define FP8BS_TILE_FPROP 128, 128, 2, 2, 2
-#endif
-#ifndef FP8BS_TILE_DGRAD
-#define FP8BS_TILE_DGRAD 128, 128, 2, 2, 2
-#endif
-#ifndef FP8BS_TILE_WGRAD
-#define FP8BS_TILE_WGRAD 128, 128, 2, 2, 2
-#endif
-#ifndef FP8BS_TILE_GROUPED
-#define FP8BS_TILE_GROUPED 128, 128, 2, 2, 2
-#endif
-// 64 x 128 tiles (4 waves of 32 x 64, 3 stages) for problems with fewer
-// 128 x 128 tiles than CUs: the output 4096x512 over a 32768-long
-// contraction (128 tiles) measured 209 -> 168 us with them.
-#ifndef FP8BS_TILE_SMALL
+// gemm_kernel tiles: 128 x 128 (2 x 2 waves of 64 x 64, 2 stages) for
+// mid-size problems, and 64 x 128 (2 x 2 waves of 32 x 64, 3 stages) for
+// problems with fewer 128 x 128 tiles than CUs: the output 4096x512 over a
+// 32768-long contraction (128 tiles) measured 209 -> 168 us with them.
+#define FP8BS_TILE_MID 128, 128, 2, 2, 2
 #define FP8BS_TILE_SMALL 64, 128, 2, 2, 3
-#endif
 // Split contraction for activation gradients with few output tiles and a long
 // contraction (dX [4096, 512] over 32768: 64 tiles of 256x128 leave three
 // quarters of the CUs idle).  ksplit workgroups per tile each run one
 // contiguous range of K slabs on the warp-specialized kernel and store an
 // FP32 partial; splitk_reduce_kernel sums the partials in split order and
-// rounds once to bf16.  The partials live in a stream-ordered allocation
-// (hipMallocAsync / hipFreeAsync on the call's stream), so calls on different
-// streams never share them.
+// rounds once to bf16.  fp8bs_gemm takes the partials from a stream-ordered
+// allocation (hipMallocAsync / hipFreeAsync on the call's stream), so calls
+// on different streams never share them; when that allocation fails it runs
+// the unsplit kernels instead.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int64_t ksplit,
                                                             int64_t m, int64_t n, uint16_t* __restrict__ c,
                                                             int64_t ldc) {
@@ -1188,18 +1177,20 @@ static int64_t dgrad_ksplit(int64_t m, int64_t n, int64_t k, int cus) {
   return ks;
 }
 
-static int launch_dgrad_split(GemmArgs a, hipStream_t s, int64_t ks) {
+static int64_t dgrad_split_bytes(int64_t m, int64_t n, int64_t ks) {
+  return ks * m * n * (int64_t)sizeof(float);
+}
+
+// Enqueue the split dgrad with its FP32 partials in `ws` (at least
+// dgrad_split_bytes(m, n, ks) bytes, not read before it is written).
+static int launch_dgrad_split(GemmArgs a, hipStream_t s, int64_t ks, float* ws) {
   a.tiles_n = a.n / 128;
   a.tiles_m = (a.m + 255) / 256;
   a.group_m = choose_group_m(a, 256, 128, 2);
   a.ksplit = ks;
+  a.ws = ws;
   const int64_t tiles = a.tiles_m * a.tiles_n;
   const int64_t groups = a.m * a.n / 4;
-  if (tiles > kMaxGrid || ks > 65535 || (groups + 255) / 256 > kMaxGrid) return FP8BS_ERR_SHAPE;
-  void* ws = nullptr;
-  if (hipMallocAsync(&ws, (size_t)ks * (size_t)a.m * (size_t)a.n * sizeof(float), s) != hipSuccess)
-    return FP8BS_ERR_LAUNCH;
-  a.ws = static_cast<float*>(ws);
   hipLaunchKernelGGL((gemm_ws_kernel<kDgrad, 8, 256, 128, false, true>), dim3((unsigned)tiles, (unsigned)ks),
                      dim3(64 * 12), 0, s, a);
   int st = launch_status();
@@ -1208,17 +1199,37 @@ static int launch_dgrad_split(GemmArgs a, hipStream_t s, int64_t ks) {
                        a.m, a.n, static_cast<uint16_t*>(a.c), a.ldc);
     st = launch_status();
   }
-  if (hipFreeAsync(ws, s) != hipSuccess && st == FP8BS_OK) st = FP8BS_ERR_LAUNCH;
   return st;
+}
+
+static bool split_grid_ok(int64_t m, int64_t n, int64_t ks) {
+  const int64_t tiles = ((m + 255) / 256) * (n / 128);
+  return tiles <= kMaxGrid && ks <= 65535 && (m * n / 4 + 255) / 256 <= kMaxGrid;
 }
 
 static bool small_tiles(int64_t m, int64_t n) {
   return ((m + 127) / 128) * ((n + 127) / 128) < cu_count();
 }
 
-extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
-                          int64_t m, int64_t n, int64_t k, int b_layout, uint16_t* c, int64_t ldc,
-                          void* stream) {
+// fp8bs_gemm without a contraction split: the warp-specialized kernel for
+// problems with enough large tiles, else gemm_kernel's mid or small tiles.
+static int gemm_unsplit(GemmArgs a, int b_layout, hipStream_t stream) {
+  const int64_t m = a.m, n = a.n;
+  if (use_ws(m, n)) {
+    if (b_layout == 0) return launch_gemm_ws<kFprop>(a, stream, cu_count());
+    return launch_gemm_ws<kDgrad>(a, stream, cu_count());
+  }
+  if (small_tiles(m, n)) {
+    if (b_layout == 0) return launch_gemm<kFprop, FP8BS_TILE_SMALL>(a, stream);
+    return launch_gemm<kDgrad, FP8BS_TILE_SMALL>(a, stream);
+  }
+  if (b_layout == 0) return launch_gemm<kFprop, FP8BS_TILE_MID>(a, stream);
+  return launch_gemm<kDgrad, FP8BS_TILE_MID>(a, stream);
+}
+
+// Argument checks of fp8bs_gemm; on success fills *a.
+static int gemm_check(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb, int64_t m,
+                      int64_t n, int64_t k, int b_layout, uint16_t* c, int64_t ldc, GemmArgs* a) {
   if (!qa || !sa || !qb || !sb || !c) return FP8BS_ERR_NULL;
   if (b_layout != 0 && b_layout != 1) return FP8BS_ERR_FLAG;
   if (m <= 0 || n <= 0 || k <= 0 || n % 128 || k % BK || ldc < n) return FP8BS_ERR_SHAPE;
@@ -1226,21 +1237,33 @@ extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb,
   if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
       ldc % 8)
     return FP8BS_ERR_ALIGN;
-  GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, k, nullptr, 0, 0, 0, 0, 0, nullptr, 1, m * n * 2 > kStreamBytes};
+  *a = GemmArgs{qa, sa, qb, sb, c, ldc, m, n, k, nullptr, 0, 0, 0, 0, 0, nullptr, 1, m * n * 2 > kStreamBytes};
+  return FP8BS_OK;
+}
+
+extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
+                          int64_t m, int64_t n, int64_t k, int b_layout, uint16_t* c, int64_t ldc,
+                          void* stream) {
+  GemmArgs a;
+  const int chk = gemm_check(qa, sa, qb, sb, m, n, k, b_layout, c, ldc, &a);
+  if (chk != FP8BS_OK) return chk;
+  hipStream_t s = (hipStream_t)stream;
   if (b_layout == 1) {
     const int64_t ks = dgrad_ksplit(m, n, k, cu_count());
-    if (ks > 1) return launch_dgrad_split(a, (hipStream_t)stream, ks);
+    if (ks > 1) {
+      if (!split_grid_ok(m, n, ks)) return FP8BS_ERR_SHAPE;
+      void* ws = nullptr;
+      if (hipMallocAsync(&ws, (size_t)dgrad_split_bytes(m, n, ks), s) == hipSuccess) {
+        int st = launch_dgrad_split(a, s, ks, static_cast<float*>(ws));
+        if (hipFreeAsync(ws, s) != hipSuccess && st == FP8BS_OK) st = FP8BS_ERR_LAUNCH;
+        return st;
+      }
+      // no memory for the partials: clear the runtime's error state and run
+      // the unsplit kernels (same result within rounding, other bits)
+      (void)hipGetLastError();
+    }
   }
-  if (use_ws(m, n)) {
-    if (b_layout == 0) return launch_gemm_ws<kFprop>(a, (hipStream_t)stream, cu_count());
-    return launch_gemm_ws<kDgrad>(a, (hipStream_t)stream, cu_count());
-  }
-  if (small_tiles(m, n)) {
-    if (b_layout == 0) return launch_gemm<kFprop, FP8BS_TILE_SMALL>(a, (hipStream_t)stream);
-    return launch_gemm<kDgrad, FP8BS_TILE_SMALL>(a, (hipStream_t)stream);
-  }
-  if (b_layout == 0) return launch_gemm<kFprop, FP8BS_TILE_FPROP>(a, (hipStream_t)stream);
-  return launch_gemm<kDgrad, FP8BS_TILE_DGRAD>(a, (hipStream_t)stream);
+  return gemm_unsplit(a, b_layout, s);
 }
 
 extern "C" int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int32_t* seg_offsets,
@@ -1257,7 +1280,7 @@ extern "C" int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int3
   GemmArgs a{qa, sa, qb, sb, c, n, total_rows, n, k, seg_offsets, num_experts, 0, 0, 0, 0, nullptr, 1,
              total_rows * n * 2 > kStreamBytes};
   if (n % 256 == 0) return launch_grouped_ws(a, (hipStream_t)stream);
-  return launch_gemm<kGrouped, FP8BS_TILE_GROUPED>(a, (hipStream_t)stream);
+  return launch_gemm<kGrouped, FP8BS_TILE_MID>(a, (hipStream_t)stream);
 }
 
 extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
@@ -1273,5 +1296,5 @@ extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_
   GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, t, nullptr, 0, 0, 0, accumulate, 0};
   if (use_ws(m, n)) return launch_gemm_ws<kWgrad>(a, (hipStream_t)stream, cu_count());
   if (small_tiles(m, n)) return launch_gemm<kWgrad, FP8BS_TILE_SMALL>(a, (hipStream_t)stream);
-  return launch_gemm<kWgrad, FP8BS_TILE_WGRAD>(a, (hipStream_t)stream);
+  return launch_gemm<kWgrad, FP8BS_TILE_MID>(a, (hipStream_t)stream);
 }

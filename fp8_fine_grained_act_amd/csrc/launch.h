@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/fp8bs.h"
 
 namespace fp8bs {
@@ -26,18 +28,20 @@ inline int launch_status() {
 // data that is.  Smaller inputs may still be cached from their producer.
 constexpr int64_t kStreamBytes = 128LL << 20;
 
-// Compute units of the current device (cached per device; persistent grids
-// and tile-shape choices are sized by it).
+// Compute units of the current device, cached per device ordinal.  Each
+// entry is an atomic, so host threads calling the library at once see either
+// 0 (and query the attribute themselves) or the device's count; the tile
+// shape, the persistent grid and the dgrad contraction split are sized by it.
 inline int cu_count() {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 }  // namespace fp8bs

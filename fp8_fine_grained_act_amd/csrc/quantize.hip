@@ -52,10 +52,9 @@ __global__ __launch_bounds__(256) void quant_act_rows_kernel(
 // along the columns.  x [T, C] -> qt [C, T], st [C, T/128]; with ROWS also
 // q [T, C], s [T, C/128] from the same read of x.
 //
-// A 256-thread block owns a strip of 128 columns and walks kQGroups squares
-// of 128 x 128 down it.  Each square (32 KB of bf16) is loaded with 8 loads of
-// 16 bytes per thread (every row segment a full 256 bytes) and staged in LDS;
-// the loads of the next square are issued before the current one is coded.
+// A 256-thread block owns one square of 128 x 128.  The square (32 KB of
+// bf16) is loaded with 8 loads of 16 bytes per thread (every row segment a
+// full 256 bytes) and staged in LDS.
 //
 // LDS: row R of the square is 256 bytes; its 16-byte chunk q sits at chunk
 // q ^ f(R), f(R) = (R & 15) ^ (((R >> 5) & 3) << 2).
@@ -76,15 +75,6 @@ __global__ __launch_bounds__(256) void quant_act_rows_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kQB = 128;                   // rows and columns per square
 
-#ifndef FP8BS_QGROUPS
-#define FP8BS_QGROUPS 1
-#endif
-#ifndef FP8BS_QORDER
-#define FP8BS_QORDER 0
-#endif
-constexpr int kQGroups = FP8BS_QGROUPS;    // squares per block, walked down the strip
-constexpr int kQOrder = FP8BS_QORDER;      // 0: blockIdx.x walks column strips, 1: row ranges
-
 __device__ __forceinline__ int qswz(int row) { return (row & 15) ^ (((row >> 5) & 3) << 2); }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -102,11 +92,8 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t tile[kQB * 256];
 
   const int tid = threadIdx.x;
-  const int64_t rblk = kQOrder ? blockIdx.x : blockIdx.y;
-  const int64_t c0 = (int64_t)(kQOrder ? blockIdx.y : blockIdx.x) * kQB;
-  const int64_t first = rblk * kQGroups * kQB;                 // rows % 128 == 0: squares are full
-  // squares of this block (at least one: rows % 128 == 0 and the grid is exact)
-  const int nsq = kQGroups == 1 ? 1 : (int)min<int64_t>(kQGroups, (rows - first) / kQB);
+  const int64_t c0 = (int64_t)blockIdx.x * kQB;               // the square's first column
+  const int64_t r0 = (int64_t)blockIdx.y * kQB;               // and first row (rows % 128 == 0: squares are full)
 
   // staging lanes: thread (chunk, rr) covers rows rr, rr+16, ... at 16-byte chunk `chunk`.
   // A chunk past the last column (cols % 8 == 0, so chunks are whole) loads a valid
@@ -114,33 +101,27 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
   const int chunk = tid & 15;
   const int rr = tid >> 4;
   const bool cok = c0 + chunk * 8 < cols;
-  const uint16_t* src = x + (first + rr) * ldx + (cok ? c0 + chunk * 8 : 0);
+  const uint16_t* src = x + (r0 + rr) * ldx + (cok ? c0 + chunk * 8 : 0);
   uint4 v[8];
-  auto load = [&](int sq) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint16_t* a = src + ((int64_t)sq * kQB + 16 * i) * ldx;
-      v[i] = STREAM ? load_nt(a) : *reinterpret_cast<const uint4*>(a);
-    }
-    if (!cok) {
+  for (int i = 0; i < 8; ++i) {
+    const uint16_t* a = src + (int64_t)(16 * i) * ldx;
+    v[i] = STREAM ? load_nt(a) : *reinterpret_cast<const uint4*>(a);
+  }
+  if (!cok) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  load(0);
+    for (int i = 0; i < 8; ++i) v[i] = make_uint4(0, 0, 0, 0);
+  }
 
   const int lane = tid & 15;                                   // lane inside its 16-lane group
   const int grp16 = tid >> 4;                                  // 16 groups
-  for (int sq = 0; sq < nsq; ++sq) {
-    const int64_t r0 = first + (int64_t)sq * kQB;
-    if (sq) __syncthreads();                                   // the previous square's LDS reads are done
+  {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = rr + 16 * i;
       *reinterpret_cast<uint4*>(&tile[row * 256 + ((chunk ^ qswz(row)) << 4)]) = v[i];
     }
     __syncthreads();
-    if (sq + 1 < nsq) load(sq + 1);                            // in flight while this square is coded
 
     // ---- transposed tiles: two column quads per 16-lane group
 #pragma unroll
@@ -202,15 +183,12 @@ __global__ __launch_bounds__(256) void quant_act_cols_kernel(
   }
 }
 
+// one block per 128 x 128 square: x walks the column strips, y the rows
 static dim3 cols_grid(int64_t rows, int64_t cols) {
-  const int64_t rb = (rows / kQB + kQGroups - 1) / kQGroups;
-  const int64_t cb = (cols + kQB - 1) / kQB;
-  return kQOrder ? dim3((unsigned)rb, (unsigned)cb) : dim3((unsigned)cb, (unsigned)rb);
+  return dim3((unsigned)((cols + kQB - 1) / kQB), (unsigned)(rows / kQB));
 }
 static bool cols_grid_ok(int64_t rows, int64_t cols) {
-  const int64_t rb = (rows / kQB + kQGroups - 1) / kQGroups;
-  const int64_t cb = (cols + kQB - 1) / kQB;
-  return kQOrder ? (cb <= 65535 && rb <= kMaxGrid) : (rb <= 65535 && cb <= kMaxGrid);
+  return rows / kQB <= 65535 && (cols + kQB - 1) / kQB <= kMaxGrid;
 }
 
 // ---------------------------------------------------------------------------

@@ -3,8 +3,20 @@
  *
  * C ABI of the library libfp8bs.so.  Every entry point takes plain device
  * pointers and sizes, enqueues its kernels on the caller's HIP stream and
- * returns at once; nothing is allocated, and the library keeps no state, so
- * calls are re-entrant and thread-safe.  The caller owns every buffer.
+ * returns at once.  The caller owns every buffer it passes.
+ *
+ * Memory and state:
+ *   - One path allocates: fp8bs_gemm with b_layout == 1, when it splits the
+ *     contraction over workgroups, takes its FP32 partials from a
+ *     stream-ordered allocation on the call's stream (hipMallocAsync, freed
+ *     with hipFreeAsync after use).  If that allocation fails it clears the
+ *     runtime's error and runs the unsplit kernels instead.
+ *   - The library caches one value per device: its compute-unit count (an
+ *     atomic per device ordinal, filled on first use).  Tile shapes and the
+ *     contraction split are chosen from it, so the bits of a bf16 dgrad
+ *     result can differ between devices with different CU counts (always
+ *     within the same error bound).
+ *   Calls are re-entrant and thread-safe.
  *
  * The method (pages cited by title and section):
  *   "DeepSeek-V3 技术报告深度解读" (sherconan.github.io), section 3 "FP8 混合精度训练":
@@ -56,7 +68,10 @@ extern "C" {
 #define FP8BS_ERR_LAUNCH (-5) /* the HIP runtime rejected a kernel launch             */
 
 /*
- * Activation quantization in 1x128 tiles (the pages' activation granularity).
+ * Activation quantization in 1x128 tiles: one FP32 scale per row and 128
+ * consecutive elements ("DeepSeek-V3 技术报告深度解读", section 3 "FP8 混合精度训练":
+ * activations are quantized per 1x128 tile; deepseek.csdn.net page, section
+ * 二(四) "FP8 低精度训练": tile-wise activations instead of per-tensor scaling).
  *
  * transpose == 0: tiles run along the columns.
  *   x       bf16 [rows, cols], row stride ldx elements
@@ -123,7 +138,9 @@ int fp8bs_requantize_act_1x128_t(const uint8_t* q, const float* scales, int64_t 
                                  int64_t ldq, uint8_t* qt, int64_t ldqt, float* scales_t, void* stream);
 
 /*
- * Weight quantization in 128x128 blocks (the pages' weight granularity).
+ * Weight quantization in 128x128 blocks: one FP32 scale per block
+ * ("DeepSeek-V3 技术报告深度解读", section 3 "FP8 混合精度训练": weights are
+ * quantized per 128x128 block; deepseek.csdn.net page, section 二(四)).
  *   w       bf16 [n, k], row stride ldw elements
  *   q       E4M3 [n, k], row stride ldq bytes
  *   scales  f32  [n/128, k/128], row-major, contiguous
@@ -138,7 +155,11 @@ int fp8bs_quantize_w_128x128(const uint16_t* w, int64_t n, int64_t k, int64_t ld
  * Block-scaled GEMM with bf16 output: C[m, n] = sum_k A[m, k] * B(k, n), the
  * contraction in 128-long blocks, each block's FP32 partial multiplied by
  * sa[m, kb] * sb(kb, n-block) and added to an FP32 accumulator; the result is
- * rounded to bf16 (nearest, ties to even).
+ * rounded to bf16 (nearest, ties to even).  The forward and the
+ * activation-gradient GEMMs run in FP8 and their partial sums move to FP32
+ * after every 128 elements of the contraction ("DeepSeek-V3 技术报告深度解读",
+ * section 3 "FP8 混合精度训练"; deepseek.csdn.net page, section 二(四): the
+ * matrix-multiply partials accumulate in FP32 registers).
  *   qa  E4M3 [m, k] contiguous,  sa f32 [m, k/128] contiguous (1x128 tiles)
  *   b_layout == 0 (forward, y = x W^T):
  *       qb E4M3 [n, k] contiguous, sb f32 [n/128, k/128] (128x128 blocks)
@@ -150,12 +171,13 @@ int fp8bs_quantize_w_128x128(const uint16_t* w, int64_t n, int64_t k, int64_t ld
  * Workspace (b_layout == 1 only): when the output's 256x128 tiles would fill
  * at most half the compute units and the contraction is long (at least 32
  * blocks), the contraction is split over workgroups.  Their FP32 partials,
- * split x m x n x 4 bytes (split <= the compute-unit count / tiles), take a
- * stream-ordered allocation on `stream` (hipMallocAsync, freed with
- * hipFreeAsync after the summing kernel).  Graph capture records both.  The
- * partials are summed in split order and rounded once, so the result is
- * deterministic but not bit-identical to an unsplit run.  FP8BS_ERR_LAUNCH if
- * the allocation fails.
+ * split x m x n x 4 bytes (split <= the compute-unit count / tiles, so at most
+ * CUs x 128 KiB), take a stream-ordered allocation on `stream`
+ * (hipMallocAsync, freed with hipFreeAsync after the summing kernel; graph
+ * capture records both).  The partials are summed in split order and rounded
+ * once: the result is deterministic for a given device and split, but not
+ * bit-identical to an unsplit run.  If the allocation fails, the runtime's
+ * error is cleared and the unsplit kernels run instead (same error bound).
  */
 int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
                int64_t m, int64_t n, int64_t k, int b_layout, uint16_t* c, int64_t ldc,
@@ -164,7 +186,11 @@ int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const floa
 /*
  * MoE grouped GEMM (forward) over expert row segments.  The rows of expert e
  * are [seg_offsets[e], seg_offsets[e+1]); each segment gets fp8bs_gemm
- * (b_layout 0) with that expert's weight.
+ * (b_layout 0) with that expert's weight.  Each token is routed to 8 of 256
+ * routed experts (deepseek.csdn.net page, section 一(二) "DeepSeekMoE 架构"),
+ * and the expert FFN GEMMs are among the GEMMs that run in FP8 with 1x128
+ * activation tiles and 128x128 weight blocks ("DeepSeek-V3 技术报告深度解读",
+ * section 3 "FP8 混合精度训练").
  *   qa          E4M3 [total_rows, k], sa f32 [total_rows, k/128]
  *   seg_offsets int32 [num_experts + 1], DEVICE memory
  *   qb          E4M3 [num_experts, n, k], sb f32 [num_experts, n/128, k/128]
@@ -188,7 +214,11 @@ int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int32_t* seg_of
 /*
  * Weight-gradient GEMM: C[m, n] (+)= sum_t A[m, t] * B[n, t] over tokens t,
  * with per-row scales on both operands (both come from
- * fp8bs_quantize_act_1x128 with transpose == 1), FP32 output.
+ * fp8bs_quantize_act_1x128 with transpose == 1), FP32 output.  The weight
+ * gradient is the third GEMM of a layer that runs in FP8
+ * ("DeepSeek-V3 技术报告深度解读", section 3 "FP8 混合精度训练"); its scale groups
+ * lie along its contraction, the tokens (a reading: the pages give only the
+ * 1x128 activation granularity).
  *   qa  E4M3 [m, t] contiguous, sa f32 [m, t/128]
  *   qb  E4M3 [n, t] contiguous, sb f32 [n, t/128]
  *   c   f32 [m, n], row stride ldc elements
