@@ -1266,6 +1266,54 @@ extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb,
   return gemm_unsplit(a, b_layout, s);
 }
 
+// ---- fp8bs_gemm without allocation -------------------------------------------
+// The split dgrad's FP32 partials live in one fixed device array per GPU.  A
+// split is chosen only when tiles x split <= CUs, so its partials take at most
+// CUs x 256 x 128 floats: 32 MiB on the 256 CUs of an MI355X.  In host code
+// the array's name stands for no device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per device
+// and kept in scratch_ptrs.  No kernel needs the array zeroed: every split
+// workgroup writes its whole partial tile before the summing kernel reads it.
+constexpr int64_t kScratchBytes = 32LL << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+static float* scratch_device_ptr() {
+  static std::atomic<float*> scratch_ptrs[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  float* ptr = scratch_ptrs[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    ptr = static_cast<float*>(q);
+    scratch_ptrs[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+extern "C" int fp8bs_gemm_noalloc(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
+                                  int64_t m, int64_t n, int64_t k, int b_layout, uint16_t* c, int64_t ldc,
+                                  void* stream) {
+  GemmArgs a;
+  const int chk = gemm_check(qa, sa, qb, sb, m, n, k, b_layout, c, ldc, &a);
+  if (chk != FP8BS_OK) return chk;
+  hipStream_t s = (hipStream_t)stream;
+  if (b_layout == 1) {
+    const int64_t ks = dgrad_ksplit(m, n, k, cu_count());
+    if (ks > 1) {
+      if (!split_grid_ok(m, n, ks)) return FP8BS_ERR_SHAPE;
+      if (dgrad_split_bytes(m, n, ks) > kScratchBytes) return FP8BS_ERR_SCRATCH;
+      float* ws = scratch_device_ptr();
+      if (ws == nullptr) return FP8BS_ERR_LAUNCH;
+      return launch_dgrad_split(a, s, ks, ws);
+    }
+  }
+  return gemm_unsplit(a, b_layout, s);
+}
+
 extern "C" int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int32_t* seg_offsets,
                                   int64_t num_experts, int64_t total_rows, const uint8_t* qb,
                                   const float* sb, int64_t n, int64_t k, uint16_t* c, void* stream) {

@@ -326,6 +326,7 @@ extern "C" const char* fp8bs_status_string(int status) {
     case FP8BS_ERR_ALIGN: return "misaligned pointer or leading dimension";
     case FP8BS_ERR_FLAG: return "unknown flag value";
     case FP8BS_ERR_LAUNCH: return "kernel launch failed";
+    case FP8BS_ERR_SCRATCH: return "problem needs more than the fixed scratch array";
     default: return "unknown status";
   }
 }

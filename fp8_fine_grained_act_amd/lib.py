@@ -28,6 +28,8 @@ _SIGNATURES = {
     "fp8bs_requantize_act_1x128_t": [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p],
     "fp8bs_gemm": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int, _c_void_p, _i64,
                    _c_void_p],
+    "fp8bs_gemm_noalloc": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int, _c_void_p, _i64,
+                           _c_void_p],
     "fp8bs_grouped_gemm": [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64, _i64,
                            _c_void_p, _c_void_p],
     "fp8bs_gemm_wgrad": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _int,
@@ -199,7 +201,7 @@ def fp8bs_quantize_w_128x128(w, q=None, scales=None, stream=None):
     return q, scales
 
 
-def fp8bs_gemm(qa, sa, qb, sb, b_layout=0, c=None, stream=None):
+def fp8bs_gemm(qa, sa, qb, sb, b_layout=0, c=None, stream=None, _entry="fp8bs_gemm"):
     """bf16 C [m, n] from E4M3 A [m, k] and B ([n, k] for b_layout 0, [k, n] for 1)."""
     for t, nm in ((qa, "qa"), (qb, "qb")):
         _dev(t, torch.uint8, nm)
@@ -215,10 +217,16 @@ def fp8bs_gemm(qa, sa, qb, sb, b_layout=0, c=None, stream=None):
         c = torch.empty((m, n), dtype=torch.bfloat16, device=qa.device)
     _dev(c, torch.bfloat16, "c")
     ldc = _row_major(c, "c")
-    st = raw.fp8bs_gemm(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(), m, n, k, int(b_layout),
-                        c.data_ptr(), ldc, _stream(stream))
-    _check("fp8bs_gemm", st)
+    st = getattr(raw, _entry)(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(), m, n, k, int(b_layout),
+                              c.data_ptr(), ldc, _stream(stream))
+    _check(_entry, st)
     return c
+
+
+def fp8bs_gemm_noalloc(qa, sa, qb, sb, b_layout=0, c=None, stream=None):
+    """fp8bs_gemm that never allocates device memory (the split dgrad uses the library's fixed array).
+    c is allocated here only when the caller passes none."""
+    return fp8bs_gemm(qa, sa, qb, sb, b_layout=b_layout, c=c, stream=stream, _entry="fp8bs_gemm_noalloc")
 
 
 def fp8bs_grouped_gemm(qa, sa, seg_offsets, qb, sb, c=None, stream=None):

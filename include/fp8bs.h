@@ -11,12 +11,15 @@
  *     stream-ordered allocation on the call's stream (hipMallocAsync, freed
  *     with hipFreeAsync after use).  If that allocation fails it clears the
  *     runtime's error and runs the unsplit kernels instead.
+ *     fp8bs_gemm_noalloc is the same call without allocation.
  *   - The library caches one value per device: its compute-unit count (an
  *     atomic per device ordinal, filled on first use).  Tile shapes and the
  *     contraction split are chosen from it, so the bits of a bf16 dgrad
  *     result can differ between devices with different CU counts (always
  *     within the same error bound).
- *   Calls are re-entrant and thread-safe.
+ *   - fp8bs_gemm_noalloc keeps its split partials in one fixed device array
+ *     per GPU (see its declaration).
+ *   Apart from that shared array, calls are re-entrant and thread-safe.
  *
  * The method (pages cited by title and section):
  *   "DeepSeek-V3 技术报告深度解读" (sherconan.github.io), section 3 "FP8 混合精度训练":
@@ -66,6 +69,7 @@ extern "C" {
 #define FP8BS_ERR_ALIGN (-3)  /* a pointer or leading dimension is misaligned         */
 #define FP8BS_ERR_FLAG (-4)   /* an enum-like flag has an unknown value               */
 #define FP8BS_ERR_LAUNCH (-5) /* the HIP runtime rejected a kernel launch             */
+#define FP8BS_ERR_SCRATCH (-6) /* needs more than fp8bs_gemm_noalloc's fixed array     */
 
 /*
  * Activation quantization in 1x128 tiles: one FP32 scale per row and 128
@@ -182,6 +186,27 @@ int fp8bs_quantize_w_128x128(const uint16_t* w, int64_t n, int64_t k, int64_t ld
 int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
                int64_t m, int64_t n, int64_t k, int b_layout, uint16_t* c, int64_t ldc,
                void* stream);
+
+/*
+ * fp8bs_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture that must record no allocation, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * fp8bs_gemm; it never allocates.  Where fp8bs_gemm would split the
+ * contraction of a dgrad (b_layout == 1), the FP32 partials go to a fixed
+ * device array of 32 MiB per GPU, part of the library's code object and held
+ * until the process ends; the split is chosen only when
+ * split x tiles <= compute units, so on a 256-CU MI355X it always fits.
+ * Every call on one GPU shares that array: calls whose split dgrads overlap in
+ * time on one GPU (other streams, other host threads) race and give wrong
+ * results; order them on one stream.  Nothing in the array needs clearing (each
+ * call writes the partials it reads).
+ * Returns FP8BS_ERR_SCRATCH, before anything is enqueued, if a split would
+ * need more than 32 MiB (devices with more than 256 compute units), and
+ * FP8BS_ERR_LAUNCH if the array's device address cannot be obtained.
+ */
+int fp8bs_gemm_noalloc(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
+                       int64_t m, int64_t n, int64_t k, int b_layout, uint16_t* c, int64_t ldc,
+                       void* stream);
 
 /*
  * MoE grouped GEMM (forward) over expert row segments.  The rows of expert e

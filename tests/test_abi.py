@@ -48,7 +48,7 @@ def test_status_strings(raw):
     from fp8_fine_grained_act_amd import lib
 
     assert lib.status_string(OK) == "ok"
-    for s in (ENULL, ESHAPE, EALIGN, EFLAG, -5):
+    for s in (ENULL, ESHAPE, EALIGN, EFLAG, -5, -6):
         assert lib.status_string(s) not in ("ok", "unknown status")
     assert lib.status_string(123) == "unknown status"
 
