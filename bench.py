@@ -255,6 +255,11 @@ def build_grouped_step(lib, rotate):
     pairs = int(counts.sum())
     x = dev_bf16(host["x"])
     seg_pad = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    # the routing's row map of this layout: each expert's routed rows, then -1 on its padding
+    rt_host = np.full(total, -1, np.int32)
+    for ex in range(len(counts)):
+        rt_host[offsets[ex]:offsets[ex] + counts[ex]] = np.arange(counts[ex], dtype=np.int32)
+    row_token = torch.from_numpy(rt_host).cuda()
     w = device_expert_weights(cfg)
     i32, u8, f32, bf16 = torch.int32, torch.uint8, torch.float32, torch.bfloat16
     e = lambda *s, dt: torch.empty(s, dtype=dt, device="cuda")  # noqa: E731
@@ -263,16 +268,18 @@ def build_grouped_step(lib, rotate):
     y = e(total, n, dt=bf16)
     state = {"i": 0}
     kb = k // 128
-    # algorithmic bytes over the padded rows (the rows the kernels read and write)
+    # algorithmic bytes: the X quantizer reads and writes every padded row; the
+    # grouped GEMM reads the routed rows of X (the row map clips the padding),
+    # the row map, every expert weight once, and writes every padded output row
     x_bytes = total * k * 3 + total * kb * 4
     w_bytes = num_e * n * k * 3 + num_e * (n // 128) * kb * 4
-    gemm_bytes = total * (k + kb * 4) + num_e * (n * k + (n // 128) * kb * 4) + total * n * 2
+    gemm_bytes = pairs * (k + kb * 4) + total * 4 + num_e * (n * k + (n // 128) * kb * 4) + total * n * 2
     calls = [
         Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, q=qx, scales=sx),
              nbytes=x_bytes, outs=(qx, sx)),
         Call("quant_w_experts", "quant", lambda: lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw),
              nbytes=w_bytes, outs=(qw, sw)),
-        Call("gemm_grouped", "gemm", lambda: lib.fp8bs_grouped_gemm(qx, sx, seg_pad, qw, sw, c=y),
+        Call("gemm_grouped", "gemm", lambda: lib.fp8bs_grouped_gemm(qx, sx, seg_pad, qw, sw, c=y, row_token=row_token),
              flops=2.0 * pairs * n * k, nbytes=gemm_bytes, outs=(y,)),
     ]
 
@@ -305,7 +312,7 @@ def build_grouped_step(lib, rotate):
                          "of the padded rows + 128x128 quantization of all 256 expert weights + grouped GEMM",
                 routed_rows=pairs, padded_rows=total, experts=num_e, N=n, K=k,
                 value_flops="grouped GEMM over the routed rows, 2*32768*4096*7168",
-                bytes_counted="padded rows")
+                bytes_counted="quantizer: padded rows; grouped GEMM: routed rows of X, padded output rows")
     data = dict(kind="c4", x=host["x"], counts=counts, offsets=offsets, w_dev=w, cfg=cfg)
     return calls, state, desc, data, extras
 

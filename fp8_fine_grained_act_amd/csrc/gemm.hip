@@ -66,7 +66,20 @@ struct GemmArgs {
   float* ws;        // split contraction: FP32 partials [ksplit][m][n] (gridDim.y = ksplit)
   int64_t ksplit;
   int stream_out;   // bf16 output larger than half the last-level cache: non-temporal stores
+  const int32_t* row_token;  // grouped: the dispatch's row map (-1: padding row), or null
 };
+
+// Rows of a 128-row grouped tile that are read: up to and including its last
+// routed row (row_token >= 0); the rows after it are padding, loaded as zeros
+// by the clipped buffer ranges with no memory traffic.  Each lane of the wave
+// checks two of the tile's 128 entries.
+__device__ __forceinline__ int64_t live_rows_128(const int32_t* rt, int lane) {
+  const int t0 = rt[2 * lane], t1 = rt[2 * lane + 1];
+  const uint64_t b0 = __ballot(t0 >= 0), b1 = __ballot(t1 >= 0);
+  const int e0 = b0 ? 2 * (63 - __clzll((long long)b0)) + 1 : 0;
+  const int e1 = b1 ? 2 * (63 - __clzll((long long)b1)) + 2 : 0;
+  return __builtin_amdgcn_readfirstlane(max(e0, e1));
+}
 
 // Workgroups are dealt to the chip's 8 XCDs round-robin by workgroup id, and
 // each XCD has its own L2.  With group_m > 0 the id is first remapped so that
@@ -263,7 +276,9 @@ void gemm_kernel(GemmArgs p) {
   }
 
   // ---- buffer resources (ranges clip ragged edges to zeros) ------------------
-  const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+  int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+  static_assert(MODE != kGrouped || BM == 128, "grouped tiles are the 128-row segment steps");
+  if (MODE == kGrouped && p.row_token) rows_a = min(rows_a, live_rows_128(p.row_token + m0, lane));
   const int64_t rows_b = N - n0 < BN ? N - n0 : BN;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.qa + m0 * K, rows_a * K);
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa + m0 * nkb, rows_a * nkb * 4);
@@ -638,7 +653,9 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
     auto set_tile = [&](int i) {
       const Origin o = tile_origin(i);
       const int64_t m0 = o.m0, n0 = o.n0;
-      const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+      int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+      static_assert(MODE != kGrouped || BM == 128, "grouped tiles are the 128-row segment steps");
+      if (MODE == kGrouped && p.row_token) rows_a = min(rows_a, live_rows_128(p.row_token + m0, lane));
       const int64_t rows_b = N - n0 < BN ? N - n0 : BN;
       const uint8_t* qb = p.qb;
       const float* sb = p.sb;
@@ -1315,18 +1332,19 @@ extern "C" int fp8bs_gemm_noalloc(const uint8_t* qa, const float* sa, const uint
 }
 
 extern "C" int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int32_t* seg_offsets,
-                                  int64_t num_experts, int64_t total_rows, const uint8_t* qb,
-                                  const float* sb, int64_t n, int64_t k, uint16_t* c, void* stream) {
+                                  const int32_t* row_token, int64_t num_experts, int64_t total_rows,
+                                  const uint8_t* qb, const float* sb, int64_t n, int64_t k, uint16_t* c,
+                                  void* stream) {
   if (!qa || !sa || !seg_offsets || !qb || !sb || !c) return FP8BS_ERR_NULL;
   if (num_experts < 1 || num_experts > 65536 || total_rows <= 0 || total_rows % 128 || n <= 0 ||
       k <= 0 || n % 128 || k % BK)
     return FP8BS_ERR_SHAPE;
   if (!fits_u32(256 * k)) return FP8BS_ERR_SHAPE;
   if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
-      !aligned(seg_offsets, 4))
+      !aligned(seg_offsets, 4) || !aligned(row_token, 4))
     return FP8BS_ERR_ALIGN;
   GemmArgs a{qa, sa, qb, sb, c, n, total_rows, n, k, seg_offsets, num_experts, 0, 0, 0, 0, nullptr, 1,
-             total_rows * n * 2 > kStreamBytes};
+             total_rows * n * 2 > kStreamBytes, row_token};
   if (n % 256 == 0) return launch_grouped_ws(a, (hipStream_t)stream);
   return launch_gemm<kGrouped, FP8BS_TILE_MID>(a, (hipStream_t)stream);
 }

@@ -30,8 +30,8 @@ _SIGNATURES = {
                    _c_void_p],
     "fp8bs_gemm_noalloc": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _int, _c_void_p, _i64,
                            _c_void_p],
-    "fp8bs_grouped_gemm": [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64, _i64,
-                           _c_void_p, _c_void_p],
+    "fp8bs_grouped_gemm": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64,
+                           _i64, _c_void_p, _c_void_p],
     "fp8bs_gemm_wgrad": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _int,
                          _c_void_p],
     "fp8bs_moe_route": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p],
@@ -229,26 +229,37 @@ def fp8bs_gemm_noalloc(qa, sa, qb, sb, b_layout=0, c=None, stream=None):
     return fp8bs_gemm(qa, sa, qb, sb, b_layout=b_layout, c=c, stream=stream, _entry="fp8bs_gemm_noalloc")
 
 
-def fp8bs_grouped_gemm(qa, sa, seg_offsets, qb, sb, c=None, stream=None):
-    """MoE grouped GEMM: bf16 C [R, n]; qb [E, n, k]; seg_offsets int32 [E+1] on the device."""
+def fp8bs_grouped_gemm(qa, sa, seg_offsets, qb, sb, c=None, stream=None, row_token=None):
+    """MoE grouped GEMM: bf16 C [R, n]; qb [E, n, k]; seg_offsets int32 [E+1] on the device.
+
+    row_token (int32 [R] on the device, the routing's row map, or None): when
+    given, each 128-row tile's rows after its last routed row are not read and
+    their outputs are 0."""
     _dev(qa, torch.uint8, "qa")
     _dev(qb, torch.uint8, "qb")
     _dev(sa, torch.float32, "sa")
     _dev(sb, torch.float32, "sb")
     _dev(seg_offsets, torch.int32, "seg_offsets")
-    for t, nm in ((qa, "qa"), (qb, "qb"), (sa, "sa"), (sb, "sb"), (seg_offsets, "seg_offsets")):
+    checked = [(qa, "qa"), (qb, "qb"), (sa, "sa"), (sb, "sb"), (seg_offsets, "seg_offsets")]
+    if row_token is not None:
+        _dev(row_token, torch.int32, "row_token")
+        checked.append((row_token, "row_token"))
+    for t, nm in checked:
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
     rows, k = qa.shape
     num_e, n = qb.shape[0], qb.shape[1]
     if seg_offsets.numel() != num_e + 1:
         raise ValueError("seg_offsets must have num_experts + 1 entries")
+    if row_token is not None and row_token.numel() != rows:
+        raise ValueError("row_token must have one entry per row of qa")
     if c is None:
         c = torch.empty((rows, n), dtype=torch.bfloat16, device=qa.device)
     _dev(c, torch.bfloat16, "c")
     if not c.is_contiguous():
         raise ValueError("c must be contiguous")
-    st = raw.fp8bs_grouped_gemm(qa.data_ptr(), sa.data_ptr(), seg_offsets.data_ptr(), num_e, rows, qb.data_ptr(),
+    st = raw.fp8bs_grouped_gemm(qa.data_ptr(), sa.data_ptr(), seg_offsets.data_ptr(),
+                                None if row_token is None else row_token.data_ptr(), num_e, rows, qb.data_ptr(),
                                 sb.data_ptr(), n, k, c.data_ptr(), _stream(stream))
     _check("fp8bs_grouped_gemm", st)
     return c

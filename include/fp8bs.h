@@ -218,6 +218,8 @@ int fp8bs_gemm_noalloc(const uint8_t* qa, const float* sa, const uint8_t* qb, co
  * section 3 "FP8 混合精度训练").
  *   qa          E4M3 [total_rows, k], sa f32 [total_rows, k/128]
  *   seg_offsets int32 [num_experts + 1], DEVICE memory
+ *   row_token   int32 [total_rows], DEVICE memory, or NULL: the row map that
+ *               fp8bs_moe_route writes (-1 marks a padding row)
  *   qb          E4M3 [num_experts, n, k], sb f32 [num_experts, n/128, k/128]
  *   c           bf16 [total_rows, n] contiguous
  *   total_rows % 128 == 0, n % 128 == 0, k % 128 == 0, 1 <= num_experts <= 65536.
@@ -228,13 +230,21 @@ int fp8bs_gemm_noalloc(const uint8_t* qa, const float* sa, const uint8_t* qb, co
  * 128-row tiles end at once and those rows of c are not written (total_rows
  * may be a capacity such as fp8bs_moe_max_rows, so that no host
  * synchronization is needed to learn the padded total).
- * Padding rows (rows of a segment beyond the expert's routed rows) are
- * expected to hold zeros in the bf16 source, so their codes and scales are
- * zero and their outputs are exactly 0.
+ * Padding rows (rows of a segment beyond the expert's routed rows):
+ *   row_token NULL: every row of a segment is read; padding rows are expected
+ *     to hold zeros in the bf16 source, so their codes and scales are zero
+ *     and their outputs are exactly 0.
+ *   row_token given: in each 128-row tile, the rows after its last row with
+ *     row_token >= 0 are not read (their codes and scales count as zero,
+ *     whatever memory holds) and their outputs are exactly 0.  The padding
+ *     then costs no memory traffic; the other rows give the same bits as
+ *     with NULL.
+ * Alignment: qa, qb, c 16-byte aligned; sa, sb, seg_offsets, row_token 4-byte.
  */
 int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int32_t* seg_offsets,
-                       int64_t num_experts, int64_t total_rows, const uint8_t* qb,
-                       const float* sb, int64_t n, int64_t k, uint16_t* c, void* stream);
+                       const int32_t* row_token, int64_t num_experts, int64_t total_rows,
+                       const uint8_t* qb, const float* sb, int64_t n, int64_t k, uint16_t* c,
+                       void* stream);
 
 /*
  * Weight-gradient GEMM: C[m, n] (+)= sum_t A[m, t] * B[n, t] over tokens t,

@@ -104,11 +104,13 @@ def test_gemm_validation(raw):
 
 def test_grouped_validation(raw):
     f = raw.fp8bs_grouped_gemm
-    assert f(P, P, None, 4, 512, P, P, 128, 128, P, None) == ENULL
-    assert f(P, P, P, 0, 512, P, P, 128, 128, P, None) == ESHAPE
-    assert f(P, P, P, 4, 500, P, P, 128, 128, P, None) == ESHAPE    # total_rows % 128
-    assert f(P, P, P, 4, 512, P, P, 128, 100, P, None) == ESHAPE
-    assert f(P, P, P + 2, 4, 512, P, P, 128, 128, P, None) == EALIGN
+    assert f(P, P, None, None, 4, 512, P, P, 128, 128, P, None) == ENULL
+    assert f(P, P, P, None, 4, 512, P, P, 128, 128, None, None) == ENULL
+    assert f(P, P, P, None, 0, 512, P, P, 128, 128, P, None) == ESHAPE
+    assert f(P, P, P, None, 4, 500, P, P, 128, 128, P, None) == ESHAPE    # total_rows % 128
+    assert f(P, P, P, None, 4, 512, P, P, 128, 100, P, None) == ESHAPE
+    assert f(P, P, P + 2, None, 4, 512, P, P, 128, 128, P, None) == EALIGN
+    assert f(P, P, P, P + 2, 4, 512, P, P, 128, 128, P, None) == EALIGN  # row_token
 
 
 def test_wgrad_validation(raw):

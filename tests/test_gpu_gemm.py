@@ -377,6 +377,43 @@ def test_grouped_empty_and_single_expert(gpu_lib):
             assert_gemm_parity(bf16_values_host(c), c64, mag, label=f"grouped n={n} offsets {off.tolist()}")
 
 
+def test_grouped_row_token_clips_padding(gpu_lib):
+    """With the row map, each 128-row tile reads its rows only up to its last
+    routed row (row_token >= 0).  Tiles with 128, 1, 2, 127, 64 and 65 live
+    rows, one routed row marked -1 inside the live run (still read: only the
+    trailing run is padding), and padding rows holding non-zero codes and
+    scales, which must not be read.  Both grouped kernels (n = 128: 128 x 128
+    tiles, n = 256: 128 x 256 warp-specialized); outputs against the oracle on
+    the inputs with the padding zeroed, and bit for bit against the call
+    without the row map on those zeroed inputs."""
+    rng = np.random.default_rng(233)
+    k, live = 384, [128, 1, 2, 127, 64, 65]
+    off = np.array([0, 256, 512, 768])                  # three experts of two tiles each
+    rows = 128 * len(live)
+    rt = np.full(rows, -1, np.int32)
+    for t, nl in enumerate(live):
+        rt[128 * t:128 * t + nl] = np.arange(nl, dtype=np.int32)
+    rt[128 * 3 + 50] = -1                                # inside tile 3's live run
+    pad = rt < 0
+    pad[128 * 3 + 50] = False
+    qa, sa = random_codes(rng, (rows, k)), random_scales(rng, (rows, k // 128))
+    qa0, sa0 = qa.copy(), sa.copy()
+    qa0[pad], sa0[pad] = 0, 0.0
+    for n in (128, 256):
+        qb, sb = random_codes(rng, (3, n, k)), random_scales(rng, (3, n // 128, k // 128))
+        seg = to_dev(off.astype(np.int32))
+        c_rt = gpu_lib.fp8bs_grouped_gemm(to_dev(qa), to_dev(sa), seg, to_dev(qb), to_dev(sb),
+                                          row_token=to_dev(rt))
+        c_zero = gpu_lib.fp8bs_grouped_gemm(to_dev(qa0), to_dev(sa0), seg, to_dev(qb), to_dev(sb))
+        assert torch.equal(c_rt.view(torch.int16), c_zero.view(torch.int16)), f"n={n}"
+        got = bf16_values_host(c_rt)
+        c64 = grouped_gemm(qa0, sa0, off, qb, sb)
+        mag = grouped_gemm(magnitude_codes(qa0), sa0, off, magnitude_codes(qb), sb)
+        assert_gemm_parity(got[~pad], c64[~pad], mag[~pad], label=f"row map n={n}")
+        assert np.all(bf16_values_host(c_rt)[pad] == 0)
+        assert np.all(c_rt.view(torch.int16).cpu().numpy()[pad] == 0)   # +0, not -0
+
+
 def test_grouped_c4_full_launch_sampled_experts(gpu_lib):
     cfg = config_by_name("c4")
     g = grouped_inputs_host(cfg, with_weights=False)
@@ -384,7 +421,15 @@ def test_grouped_c4_full_launch_sampled_experts(gpu_lib):
     w = device_expert_weights(cfg)                                 # [256, 4096, 7168] bf16 on the GPU
     qa, sa = gpu_lib.fp8bs_quantize_act_1x128(to_dev_bf16(g["x"]))
     qb, sb = gpu_lib.fp8bs_quantize_w_128x128(w)
-    c = gpu_lib.fp8bs_grouped_gemm(qa, sa, to_dev(off.astype(np.int32)), qb, sb)
+    seg = to_dev(off.astype(np.int32))
+    c = gpu_lib.fp8bs_grouped_gemm(qa, sa, seg, qb, sb)
+    # with the row map (the bench's launch): the same bits over every row
+    rt = np.full(int(off[-1]), -1, np.int32)
+    for e in range(len(counts)):
+        rt[off[e]:off[e] + counts[e]] = np.arange(counts[e], dtype=np.int32)
+    c_rt = gpu_lib.fp8bs_grouped_gemm(qa, sa, seg, qb, sb, row_token=to_dev(rt))
+    assert torch.equal(c_rt.view(torch.int16), c.view(torch.int16))
+    del c_rt
     torch.cuda.synchronize()
     order = np.argsort(counts)
     experts = sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2]), 17})

@@ -111,7 +111,7 @@ def test_moe_forward_graph_replays_match_eager(gpu_lib):
         gpu_lib.fp8bs_moe_route(ids, 16, rows_cap=cap, seg_offsets=seg, slot_rows=slot, row_token=tok)
         gpu_lib.fp8bs_moe_permute_quantize(x, slot, seg, tok, q=q, scales=s)
         gpu_lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw)
-        gpu_lib.fp8bs_grouped_gemm(q, s, seg, qw, sw, c=y)
+        gpu_lib.fp8bs_grouped_gemm(q, s, seg, qw, sw, c=y, row_token=tok)
         gpu_lib.fp8bs_moe_combine(y, slot, gates, out=out)
 
     moe_pass()

@@ -207,7 +207,8 @@ def test_combine_moe_workload_sampled(gpu_lib):
 
 @pytest.mark.parametrize("n", [128, 256])
 def test_dispatch_grouped_combine_chain(gpu_lib, n):
-    """Route -> payload -> grouped GEMM over the row capacity -> combine, against the oracle chain.
+    """Route -> payload -> grouped GEMM over the row capacity (with the route's row map) -> combine,
+    against the oracle chain.
 
     The grouped GEMM runs over the capacity (no host read of the padded total):
     its rows past the padded total must stay untouched.  n = 128 runs the
@@ -222,7 +223,7 @@ def test_dispatch_grouped_combine_chain(gpu_lib, n):
     qw, sw = gpu_lib.fp8bs_quantize_w_128x128(to_dev_bf16(w))
     cap = tok.numel()
     y = torch.full((cap, n), 77.0, dtype=torch.bfloat16, device="cuda")
-    gpu_lib.fp8bs_grouped_gemm(q, s, seg, qw, sw, c=y)
+    gpu_lib.fp8bs_grouped_gemm(q, s, seg, qw, sw, c=y, row_token=tok)
     out = gpu_lib.fp8bs_moe_combine(y, slot, to_dev(d["gates"]))
     torch.cuda.synchronize()
     r = moe_route(d["ids"], 9)
