@@ -86,6 +86,9 @@ def parse_args():
     p.add_argument("--act-cache", action="store_true",
                    help="FP8 activation caching (c2, c3, c5): X is kept as its forward 1x128 tiles and the "
                         "weight gradient's tiles along the tokens are re-tiled from them")
+    p.add_argument("--c4-two-calls", action="store_true",
+                   help="c4: quantize the expert weights and run the grouped GEMM as two calls instead of the "
+                        "grouped GEMM that quantizes its bf16 weights itself")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 512 MiB device-to-device copies (reference for HBM byte counters)")
     a = p.parse_args()
@@ -230,12 +233,16 @@ def build_layer_step(lib, cfg_name, rotate, dual=True, act_cache=False):
     return calls, state, desc, dict(d, kind="layer", cfg=cfg), []
 
 
-def build_grouped_step(lib, rotate):
+def build_grouped_step(lib, rotate, fused=True):
     """Calls of configuration c4: the MoE expert grouped GEMM with its quantization.
 
     The step: quantize X (1x128 tiles over the padded expert-major rows; the
-    padding rows are +0.0) -> quantize every expert's weight (128x128 blocks)
-    -> grouped GEMM over the padded total.  The MoE routing layout, the
+    padding rows are +0.0) -> quantize every expert's weight (128x128 blocks,
+    codes and scales stored) -> grouped GEMM over the padded total.  By
+    default the last two are one call, fp8bs_grouped_gemm_bf16w, whose copy
+    waves code each weight block where the GEMM reads it and store the codes
+    once per expert; with fused=False they are fp8bs_quantize_w_128x128 and
+    fp8bs_grouped_gemm (the same bits).  The MoE routing layout, the
     dispatch payload (permute + 1x128 quantize from token order) and the
     combine (gate-weighted sum of each token's k expert rows, [capacity, 7168]
     bf16 expert outputs drawn once on the device) are returned as extra calls:
@@ -274,14 +281,28 @@ def build_grouped_step(lib, rotate):
     x_bytes = total * k * 3 + total * kb * 4
     w_bytes = num_e * n * k * 3 + num_e * (n // 128) * kb * 4
     gemm_bytes = pairs * (k + kb * 4) + total * 4 + num_e * (n * k + (n // 128) * kb * 4) + total * n * 2
-    calls = [
-        Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, q=qx, scales=sx),
-             nbytes=x_bytes, outs=(qx, sx)),
-        Call("quant_w_experts", "quant", lambda: lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw),
-             nbytes=w_bytes, outs=(qw, sw)),
-        Call("gemm_grouped", "gemm", lambda: lib.fp8bs_grouped_gemm(qx, sx, seg_pad, qw, sw, c=y, row_token=row_token),
-             flops=2.0 * pairs * n * k, nbytes=gemm_bytes, outs=(y,)),
-    ]
+    # fused: the bf16 weights read once, their codes and scales written once,
+    # the routed rows of X and the row map read, every padded output row written
+    fused_bytes = (num_e * n * k * 2 + num_e * n * k + num_e * (n // 128) * kb * 4 + pairs * (k + kb * 4)
+                   + total * 4 + total * n * 2)
+    quant_x = Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, q=qx, scales=sx),
+                   nbytes=x_bytes, outs=(qx, sx))
+    if fused:
+        calls = [
+            quant_x,
+            Call("gemm_grouped_bf16w", "gemm",
+                 lambda: lib.fp8bs_grouped_gemm_bf16w(qx, sx, seg_pad, w, c=y, qw=qw, sw=sw, row_token=row_token),
+                 flops=2.0 * pairs * n * k, nbytes=fused_bytes, outs=(y, qw, sw)),
+        ]
+    else:
+        calls = [
+            quant_x,
+            Call("quant_w_experts", "quant", lambda: lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw),
+                 nbytes=w_bytes, outs=(qw, sw)),
+            Call("gemm_grouped", "gemm",
+                 lambda: lib.fp8bs_grouped_gemm(qx, sx, seg_pad, qw, sw, c=y, row_token=row_token),
+                 flops=2.0 * pairs * n * k, nbytes=gemm_bytes, outs=(y,)),
+        ]
 
     # the MoE kernels around the grouped GEMM (timed on their own)
     d = moe_dispatch_inputs(cfg)
@@ -307,12 +328,15 @@ def build_grouped_step(lib, rotate):
         Call("moe_combine", "moe", lambda: lib.fp8bs_moe_combine(y_down, slot, gates, out=out),
              nbytes=pairs * k * 2 + tokens * topk * 8 + tokens * k * 2, outs=(out,)),
     ]
+    step = ("1x128 quantization of the padded rows + grouped GEMM from the bf16 expert weights, each 128x128 "
+            "weight block quantized in the GEMM and its codes and scales stored once per expert" if fused else
+            "1x128 quantization of the padded rows + 128x128 quantization of all 256 expert weights + grouped GEMM")
     desc = dict(workload="c4: MoE expert grouped GEMM, 4096 tokens x top-8 of 256 experts (Zipf 1.1 counts, "
-                         "rows padded to 128 per expert), fused gate+up N=4096, K=7168; step = 1x128 quantization "
-                         "of the padded rows + 128x128 quantization of all 256 expert weights + grouped GEMM",
+                         "rows padded to 128 per expert), fused gate+up N=4096, K=7168; step = " + step,
                 routed_rows=pairs, padded_rows=total, experts=num_e, N=n, K=k,
                 value_flops="grouped GEMM over the routed rows, 2*32768*4096*7168",
-                bytes_counted="quantizer: padded rows; grouped GEMM: routed rows of X, padded output rows")
+                bytes_counted="X quantizer: padded rows; grouped GEMM: routed rows of X, padded output rows"
+                              + ("; bf16 weights read once, codes written once" if fused else ""))
     data = dict(kind="c4", x=host["x"], counts=counts, offsets=offsets, w_dev=w, cfg=cfg)
     return calls, state, desc, data, extras
 
@@ -676,7 +700,7 @@ def main():
         calls, state, desc, data, extras = build_layer_step(lib, args.config, args.rotate,
                                                             dual=not args.separate_quant, act_cache=args.act_cache)
     elif args.config == "c4":
-        calls, state, desc, data, extras = build_grouped_step(lib, args.rotate)
+        calls, state, desc, data, extras = build_grouped_step(lib, args.rotate, fused=not args.c4_two_calls)
     else:
         calls, state, desc, data, extras = build_wgrad_step(lib, args.rotate, act_cache=args.act_cache)
     if args.act_cache:

@@ -43,6 +43,8 @@
 //     and odd lanes at the same rows of columns n+8..n+15 leaves lane i with 8
 //     consecutive k of column n + i.
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -67,7 +69,22 @@ struct GemmArgs {
   int64_t ksplit;
   int stream_out;   // bf16 output larger than half the last-level cache: non-temporal stores
   const int32_t* row_token;  // grouped: the dispatch's row map (-1: padding row), or null
+  const uint16_t* w16;       // grouped from bf16 weights: w [experts, n, k] bf16
+  uint8_t* qw;               // and their codes / scales written once per expert, or null
+  float* sw;
+  int tile_sel;              // grouped: 0 every tile, 1 only each expert's first m-tile, 2 the others
 };
+
+// Expert whose segment holds row m0: the largest e with seg[e] <= m0 (empty
+// segments before it share its start and are passed over).
+__device__ __forceinline__ int grouped_expert(const GemmArgs& p, int64_t m0) {
+  int lo = 0, hi = (int)p.num_experts;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)p.seg[mid] <= m0) lo = mid; else hi = mid - 1;
+  }
+  return min(lo, (int)p.num_experts - 1);
+}
 
 // Rows of a 128-row grouped tile that are read: up to and including its last
 // routed row (row_token >= 0); the rows after it are padding, loaded as zeros
@@ -545,6 +562,184 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Copy waves of the grouped GEMM whose expert weights arrive in bf16.
+//
+// A slab unit (k-block kb of the tile) holds the A slab and its row scales,
+// copied by DMA as in the FP8 path (each copy wave a quarter), and the tile's
+// 256 weight rows n0 .. n0 + 255 over the same 128 columns: two 128 x 128
+// weight blocks, coded here with the arithmetic of quant_w_kernel (the same
+// block amax, group_scale and quant4_path), so the codes and scales equal the
+// 128x128 block quantizer's bit for bit.  Copy wave c codes rows 64c .. 64c +
+// 63, half (c & 1) of block c >> 1.  Lane (r4, j) = (lane / 16, lane % 16)
+// holds rows 64c + r4 + 4i (i < 16), bf16 columns 8j .. 8j + 7: one 16-byte
+// load per row, 4 rows' 256 contiguous bytes per load instruction; its 8
+// codes of a row go to half j % 2 of LDS chunk j / 2 (the swz layout the DMA
+// writes), and the weight-column scales of the slab to sb.
+//
+// A block's scale needs the amax of both halves.  Each wave writes its half's
+// maximum to LDS one barrier before the block is coded: the maxima of unit
+// v + 1 are written before barrier v (the barrier that publishes unit v), and
+// both waves code unit v + 1 between barriers v and v + 1.  A wave so holds
+// the bf16 of two units (2 x 64 VGPRs): unit v + 1 being coded while unit
+// v + 2 loads.  One barrier more than the FP8 path, before barrier 0, lets
+// the maxima of unit 0 cross; the MFMA waves pass it too.
+//
+// The expert's first tile (the one at its segment start) also stores the
+// codes and block scales to qw / sw, so the weights of every expert with rows
+// are coded once in memory for the GEMMs that follow (the backward's dgrad).
+// ---------------------------------------------------------------------------
+template <int BM, int BN>
+__device__ __forceinline__ void copy_waves_bf16_weights(const GemmArgs& p, int c, int lane, int units,
+                                                        int64_t m0, int64_t n0, Stage<BM, BN>& st0,
+                                                        Stage<BM, BN>& st1, Stage<BM, BN>& st2) {
+  static_assert(BM == 128 && BN == 256, "two weight blocks per slab, one 64-row half per copy wave");
+  __shared__ uint32_t half_amax[2][4];         // [unit parity][copy wave]
+  const int64_t M = p.m, N = p.n, K = p.k;
+  const int nkb = (int)(K / BK);
+  constexpr int A_CP = BM / 8 / 4, SA_JOBS = BM / 64;
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+  const int e = grouped_expert(p, m0);
+  int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+  if (p.row_token) rows_a = min(rows_a, live_rows_128(p.row_token + m0, lane));
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.qa + m0 * K, rows_a * K);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sa + m0 * nkb, rows_a * nkb * 4);
+  const int crow = 8 * c + (lane >> 3);
+  const uint32_t voff_a = (uint32_t)(crow * K + (((lane & 7) ^ swz_h(crow)) << 4));
+  const uint32_t voff_sa = (uint32_t)((64 * c + lane) * nkb) * 4u;
+
+  const int j = lane & 15;
+  const int wrow = 64 * c + (lane >> 4);       // the lane's first weight row in the tile
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w16 + ((int64_t)e * N + n0) * K, (int64_t)BN * K * 2);
+  const uint32_t voff_w = (uint32_t)((wrow * K + 8 * j) * 2);
+  const bool store_q = p.qw != nullptr && m0 == (int64_t)p.seg[e];
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qw + ((int64_t)e * N + n0) * K, store_q ? (int64_t)BN * K : 0);
+  const uint32_t voff_q = (uint32_t)(wrow * K + 8 * j);
+
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // bf16 weights are read once per tile: loads with the non-temporal hint
+  // (and so are the code stores), which keeps the re-read A rows in the caches
+  constexpr int kNT = 2;
+  auto load_row = [&](int kb, int i) -> uint4 {
+    const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)voff_w, (4 * i * (int)K + kb * BK) * 2, kNT);
+    return make_uint4(t.x, t.y, t.z, t.w);
+  };
+  auto load_w = [&](int kb, uint4 (&b)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b[i] = load_row(kb, i);
+  };
+  auto issue_a = [&](int kb, Stage<BM, BN>& s) {
+    const uint32_t ks = (uint32_t)kb * BK;
+#pragma unroll
+    for (int i = 0; i < A_CP; ++i)                                  // A copies j = c + 4i
+      dma16(ra, s.a + (c + 4 * i) * 1024, voff_a, ks + (uint32_t)(32 * i) * (uint32_t)K);
+    if (c < SA_JOBS) dma4(rsa, s.sa + 64 * c, voff_sa, (uint32_t)kb * 4u);
+  };
+  auto post_half_max = [&](int kb, const uint4 (&b)[16]) {
+    constexpr uint32_t kMag = 0x7FFF7FFFu;
+    uint32_t m2 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      m2 = max_u16x2(m2, max_u16x2(max_u16x2(b[i].x & kMag, b[i].y & kMag), max_u16x2(b[i].z & kMag, b[i].w & kMag)));
+    const uint32_t m = wave_max_u32(max(m2 & 0xFFFFu, m2 >> 16));
+    if (lane == 0) half_amax[kb & 1][c] = m;
+  };
+  // quant4_path with the tiny-tile factor as a multiplier (1 or 2^64): one
+  // code path for both (a product with 1 is exact, so the codes are the same)
+  auto quant4 = [&](uint32_t x01, uint32_t x23, const GroupScale& gs, float mul) -> uint32_t {
+    const uint32_t m01 = x01 & 0x7FFF7FFFu, m23 = x23 & 0x7FFF7FFFu;
+    const float a[4] = {bf16_lo(m01), bf16_hi(m01), bf16_lo(m23), bf16_hi(m23)};
+    float qv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float ai = a[t] * mul;
+      const float q0 = ai * gs.r;
+      const float er = __builtin_fmaf(-q0, gs.d, ai);
+      qv[t] = __builtin_fmaf(er, gs.r, q0);
+    }
+    int d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+    d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], d, true);
+    return (uint32_t)d | (__builtin_amdgcn_perm(x23, x01, 0x07050301u) & 0x80808080u);
+  };
+  // code unit kb from b into stage s; with LOAD, load rows 2i, 2i + 1 of unit
+  // kn into next beside the coding of row i < 8 (the loads go out in the first
+  // half of the coding, so most of their latency passes under the second)
+  auto code = [&](auto load_tag, int kb, const uint4 (&b)[16], Stage<BM, BN>& s, uint4 (&next)[16], int kn) {
+    constexpr bool LOAD = decltype(load_tag)::value;
+    const GroupScale gs = group_scale(max(half_amax[kb & 1][c], half_amax[kb & 1][c ^ 1]));
+    const float mul = gs.slow ? kTinyScale : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (LOAD && i < 8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) next[2 * i + h] = load_row(kn, 2 * i + h);
+      }
+      const int row = wrow + 4 * i;
+      uint2 o;
+      o.x = quant4(b[i].x, b[i].y, gs, mul);
+      o.y = quant4(b[i].z, b[i].w, gs, mul);
+      *reinterpret_cast<uint2*>(s.b + row * BK + (((j >> 1) ^ swz_h(row)) << 4) + ((j & 1) << 3)) = o;
+      if (store_q) {
+        const u32x2_t w2 = {o.x, o.y};
+        __builtin_amdgcn_raw_buffer_store_b64(w2, rq, (int)voff_q, 4 * i * (int)K + kb * BK, kNT);
+      }
+      __builtin_amdgcn_sched_barrier(0);       // keep row i's load beside row i's coding
+    }
+    s.sb[64 * c + lane] = gs.s;
+    if (store_q && (c & 1) == 0 && lane == 0)
+      p.sw[((int64_t)e * (N / 128) + n0 / 128 + (c >> 1)) * nkb + kb] = gs.s;
+  };
+
+  uint4 b0[16], b1[16];
+  // prologue: unit 0 loaded, its maxima cross the extra barrier
+  load_w(0, b0);
+  issue_a(0, st0);
+  wait_vmcnt<0>();
+  post_half_max(0, b0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): the maximum is in LDS
+  barrier();
+  // phase v, between barriers v and v + 1 (phase -1 ends at barrier 0): start
+  // unit v + 2 (weights into the registers unit v left, A into the stage slab
+  // v - 1 left), code unit v + 1, post the maxima of unit v + 2
+  // the stage of unit v (wave-uniform: a scalar select between the three)
+  auto stage = [&](int v) -> Stage<BM, BN>& {
+    const int r = v % 3;
+    return r == 0 ? st0 : (r == 1 ? st1 : st2);
+  };
+  auto phase = [&](int v, const uint4 (&b_code)[16], uint4 (&b_load)[16]) {
+    if (v + 2 < units && v + 1 < units) {
+      // the loads of unit v + 2 between the rows of unit v + 1's coding: a
+      // wave that issues its 16 loads at once is held by the queue of the
+      // CU's address unit, and its coding would wait behind them (256
+      // experts of 4096 x 7168, codes stored: 6.66 ms all at once, 5.92 ms
+      // one load per row, 5.6 ms two per row over the first 8 rows with the
+      // non-temporal hint)
+      issue_a(v + 2, stage(v + 2));
+      code(std::true_type{}, v + 1, b_code, stage(v + 1), b_load, v + 2);
+    } else {
+      if (v + 2 < units) {
+        load_w(v + 2, b_load);
+        issue_a(v + 2, stage(v + 2));
+      }
+      if (v + 1 < units) code(std::false_type{}, v + 1, b_code, stage(v + 1), b_load, 0);
+    }
+    wait_vmcnt<0>();
+    if (v + 2 < units) post_half_max(v + 2, b_load);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    barrier();                                 // barrier v + 1
+  };
+  for (int v = -1; v < units; v += 2) {        // the register buffers alternate
+    phase(v, b0, b1);
+    if (v + 1 < units) phase(v + 1, b1, b0);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Warp-specialized tiles: MW MFMA waves (4 or 8) + 4 copy waves.
 //
 // Measured on gfx950: a copy of 1 KB (buffer_load ... lds or a plain vector
@@ -573,7 +768,7 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // activation-gradient B slab is stored as copied ([k][n], swz_t layout) and
 // gathered with ds_read_b64_tr_b8 as in gemm_kernel.
 // ---------------------------------------------------------------------------
-template <int MODE, int MW, int BM, int BN, bool PERSIST, bool SPLIT = false>
+template <int MODE, int MW, int BM, int BN, bool PERSIST, bool SPLIT = false, bool W16 = false>
 __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   // MW MFMA waves: 4 (one per SIMD) or 8 (two per SIMD, so one wave's fold
   // VALU work runs under the other's MFMAs; register budget 168 per lane for
@@ -598,6 +793,8 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
                     ((BN == 256 || BN == 192) && BM == 128 && MODE != kDgrad),
                 "tile shape");
   static_assert(WAVES_M * WAVES_N == MW && WM % 16 == 0, "whole MFMA tiles per wave");
+  static_assert(!W16 || (MODE == kGrouped && !PERSIST && !SPLIT && BM == 128 && BN == 256 && MW == 8),
+                "bf16 weights: grouped 128 x 256 tiles");
 
   Stage<BM, BN>& st0 = lds_stage<BM, BN, 0>();
   Stage<BM, BN>& st1 = lds_stage<BM, BN, 1>();
@@ -641,10 +838,21 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   // leaves before its first barrier and writes nothing
   static_assert(!(MODE == kGrouped && PERSIST), "grouped tiles are one per workgroup");
   if (MODE == kGrouped && tile_origin(0).m0 >= (int64_t)p.seg[p.num_experts]) return;
+  // grouped, split in two launches: the workgroups of the other launch's tiles
+  // leave here too (an expert's first m-tile starts at its segment start)
+  if (MODE == kGrouped && p.tile_sel != 0) {
+    const int64_t m0 = tile_origin(0).m0;
+    const bool first = (int64_t)p.seg[grouped_expert(p, m0)] == m0;
+    if (first != (p.tile_sel == 1)) return;
+  }
 
   if (wave >= MW) {
     // ======================= copy waves ==========================================
     const int c = wave - MW;
+    if constexpr (W16) {
+      copy_waves_bf16_weights<BM, BN>(p, c, lane, units, tile_origin(0).m0, tile_origin(0).n0, st0, st1, st2);
+      return;
+    }
     // per-tile copy state: buffer resources (ranges clip ragged edges to zeros)
     // and the weight-scale offset of this wave's columns
     __amdgpu_buffer_rsrc_t ra, rsa, rb, rsb;
@@ -884,6 +1092,7 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   // 16 transposing LDS reads, more than one group's MFMAs hide, and it
   // measured 7% slower with the early head.
   constexpr bool kEarly = MODE != kDgrad;
+  if (W16) barrier();                          // the copy waves' exchange of slab 0's block maxima
   Head hd;
   if (kEarly) {
     barrier();                                 // slab 0 landed
@@ -1117,6 +1326,7 @@ static int launch_gemm_ws(GemmArgs a, hipStream_t s, int cus) {
 
 // Grouped GEMM on 128 x 256 tiles (n % 256 == 0), 8 MFMA waves, row-major
 // tile order (see launch_gemm).
+template <bool W16 = false>
 static int launch_grouped_ws(GemmArgs a, hipStream_t s) {
   a.tiles_n = a.n / 256;
   a.tiles_m = a.m / 128;
@@ -1125,7 +1335,8 @@ static int launch_grouped_ws(GemmArgs a, hipStream_t s) {
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
   // one tile per workgroup: the persistent form measured 9% slower here
   // (256 experts of 4096x7168), its in-loop store spilling registers
-  hipLaunchKernelGGL((gemm_ws_kernel<kGrouped, 8, 128, 256, false>), dim3((unsigned)grid), dim3(64 * 12), 0, s, a);
+  hipLaunchKernelGGL((gemm_ws_kernel<kGrouped, 8, 128, 256, false, false, W16>), dim3((unsigned)grid),
+                     dim3(64 * 12), 0, s, a);
   return launch_status();
 }
 
@@ -1347,6 +1558,37 @@ extern "C" int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int3
              total_rows * n * 2 > kStreamBytes, row_token};
   if (n % 256 == 0) return launch_grouped_ws(a, (hipStream_t)stream);
   return launch_gemm<kGrouped, FP8BS_TILE_MID>(a, (hipStream_t)stream);
+}
+
+extern "C" int fp8bs_grouped_gemm_bf16w(const uint8_t* qa, const float* sa, const int32_t* seg_offsets,
+                                        const int32_t* row_token, int64_t num_experts, int64_t total_rows,
+                                        const uint16_t* w, int64_t n, int64_t k, uint16_t* c, uint8_t* qw,
+                                        float* sw, void* stream) {
+  if (!qa || !sa || !seg_offsets || !w || !c || (qw == nullptr) != (sw == nullptr)) return FP8BS_ERR_NULL;
+  if (num_experts < 1 || num_experts > 65536 || total_rows <= 0 || total_rows % 128 || n <= 0 ||
+      k <= 0 || n % 256 || k % BK)
+    return FP8BS_ERR_SHAPE;
+  if (!fits_u32(256 * k * 2)) return FP8BS_ERR_SHAPE;
+  if (!aligned(qa, 16) || !aligned(w, 16) || !aligned(c, 16) || !aligned(qw, 16) || !aligned(sa, 4) ||
+      !aligned(sw, 4) || !aligned(seg_offsets, 4) || !aligned(row_token, 4))
+    return FP8BS_ERR_ALIGN;
+  GemmArgs a{qa, sa, nullptr, nullptr, c, n, total_rows, n, k, seg_offsets, num_experts, 0, 0, 0, 0, nullptr, 1,
+             total_rows * n * 2 > kStreamBytes, row_token, w, qw, sw, 0};
+  if (!qw) return launch_grouped_ws<true>(a, (hipStream_t)stream);
+  // With the codes stored: each expert's first m-tile codes the expert's
+  // weights from bf16 (each weight read once) and stores them; then the
+  // expert's other m-tiles read the stored codes, as fp8bs_grouped_gemm would.
+  a.tile_sel = 1;
+  const int st = launch_grouped_ws<true>(a, (hipStream_t)stream);
+  if (st != FP8BS_OK) return st;
+  GemmArgs b = a;
+  b.qb = qw;
+  b.sb = sw;
+  b.w16 = nullptr;
+  b.qw = nullptr;
+  b.sw = nullptr;
+  b.tile_sel = 2;
+  return launch_grouped_ws<false>(b, (hipStream_t)stream);
 }
 
 extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,

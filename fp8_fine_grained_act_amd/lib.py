@@ -32,6 +32,8 @@ _SIGNATURES = {
                            _c_void_p],
     "fp8bs_grouped_gemm": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64,
                            _i64, _c_void_p, _c_void_p],
+    "fp8bs_grouped_gemm_bf16w": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _i64, _i64,
+                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "fp8bs_gemm_wgrad": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _int,
                          _c_void_p],
     "fp8bs_moe_route": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p],
@@ -262,6 +264,52 @@ def fp8bs_grouped_gemm(qa, sa, seg_offsets, qb, sb, c=None, stream=None, row_tok
                                 None if row_token is None else row_token.data_ptr(), num_e, rows, qb.data_ptr(),
                                 sb.data_ptr(), n, k, c.data_ptr(), _stream(stream))
     _check("fp8bs_grouped_gemm", st)
+    return c
+
+
+def fp8bs_grouped_gemm_bf16w(qa, sa, seg_offsets, w, c=None, qw=None, sw=None, stream=None, row_token=None):
+    """MoE grouped GEMM from bf16 expert weights w [E, n, k]: bf16 C [R, n], the same bits as
+    fp8bs_grouped_gemm over fp8bs_quantize_w_128x128(w).
+
+    qw (uint8 [E, n, k]) and sw (float32 [E, n/128, k/128]), both or neither: when given, the
+    weight codes and scales of every expert that owns rows are stored there."""
+    _dev(qa, torch.uint8, "qa")
+    _dev(sa, torch.float32, "sa")
+    _dev(w, torch.bfloat16, "w")
+    _dev(seg_offsets, torch.int32, "seg_offsets")
+    checked = [(qa, "qa"), (sa, "sa"), (w, "w"), (seg_offsets, "seg_offsets")]
+    if row_token is not None:
+        _dev(row_token, torch.int32, "row_token")
+        checked.append((row_token, "row_token"))
+    if (qw is None) != (sw is None):
+        raise ValueError("qw and sw go together")
+    if qw is not None:
+        _dev(qw, torch.uint8, "qw")
+        _dev(sw, torch.float32, "sw")
+        checked += [(qw, "qw"), (sw, "sw")]
+    for t, nm in checked:
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    rows, k = qa.shape
+    if w.dim() != 3 or w.shape[2] != k:
+        raise ValueError("w must be [experts, n, k] with the k of qa")
+    num_e, n = w.shape[0], w.shape[1]
+    if seg_offsets.numel() != num_e + 1:
+        raise ValueError("seg_offsets must have num_experts + 1 entries")
+    if row_token is not None and row_token.numel() != rows:
+        raise ValueError("row_token must have one entry per row of qa")
+    if qw is not None and (tuple(qw.shape) != tuple(w.shape) or tuple(sw.shape) != (num_e, n // GROUP, k // GROUP)):
+        raise ValueError("qw must be [E, n, k] and sw [E, n/128, k/128]")
+    if c is None:
+        c = torch.empty((rows, n), dtype=torch.bfloat16, device=qa.device)
+    _dev(c, torch.bfloat16, "c")
+    if not c.is_contiguous():
+        raise ValueError("c must be contiguous")
+    st = raw.fp8bs_grouped_gemm_bf16w(qa.data_ptr(), sa.data_ptr(), seg_offsets.data_ptr(),
+                                      None if row_token is None else row_token.data_ptr(), num_e, rows,
+                                      w.data_ptr(), n, k, c.data_ptr(), None if qw is None else qw.data_ptr(),
+                                      None if sw is None else sw.data_ptr(), _stream(stream))
+    _check("fp8bs_grouped_gemm_bf16w", st)
     return c
 
 

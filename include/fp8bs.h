@@ -247,6 +247,30 @@ int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int32_t* seg_of
                        void* stream);
 
 /*
+ * MoE grouped GEMM from bf16 expert weights: fp8bs_quantize_w_128x128 of w
+ * followed by fp8bs_grouped_gemm, in one kernel.  The expert weights are
+ * quantized in 128x128 blocks for the FP8 GEMM ("DeepSeek-V3 技术报告深度解读",
+ * section 3 "FP8 混合精度训练"); here each block is coded where the GEMM
+ * reads it, so the FP8 weights are not read back from memory.
+ *   w    bf16 [num_experts, n, k] contiguous
+ *   qw   E4M3 [num_experts, n, k] and sw f32 [num_experts, n/128, k/128], or
+ *        both NULL: the codes and scales of every expert that owns at least
+ *        one row are stored (once, by its first 128-row tile), bit for bit
+ *        those of fp8bs_quantize_w_128x128(w); the blocks of experts without
+ *        rows are not written.
+ *   qa, sa, seg_offsets, row_token, num_experts, total_rows, c: as for
+ *        fp8bs_grouped_gemm, whose preconditions hold here too; n % 256 == 0.
+ * c equals, bit for bit, fp8bs_grouped_gemm over the codes and scales that
+ * fp8bs_quantize_w_128x128(w) gives.
+ * Alignment: qa, w, qw, c 16-byte aligned; sa, sw, seg_offsets, row_token
+ * 4-byte.  Errors: FP8BS_ERR_NULL also when exactly one of qw, sw is NULL.
+ */
+int fp8bs_grouped_gemm_bf16w(const uint8_t* qa, const float* sa, const int32_t* seg_offsets,
+                             const int32_t* row_token, int64_t num_experts, int64_t total_rows,
+                             const uint16_t* w, int64_t n, int64_t k, uint16_t* c, uint8_t* qw,
+                             float* sw, void* stream);
+
+/*
  * Weight-gradient GEMM: C[m, n] (+)= sum_t A[m, t] * B[n, t] over tokens t,
  * with per-row scales on both operands (both come from
  * fp8bs_quantize_act_1x128 with transpose == 1), FP32 output.  The weight

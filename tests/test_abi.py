@@ -113,6 +113,17 @@ def test_grouped_validation(raw):
     assert f(P, P, P, P + 2, 4, 512, P, P, 128, 128, P, None) == EALIGN  # row_token
 
 
+def test_grouped_bf16w_validation(raw):
+    f = raw.fp8bs_grouped_gemm_bf16w
+    assert f(P, P, P, None, 4, 512, None, 256, 128, P, None, None, None) == ENULL      # w
+    assert f(P, P, P, None, 4, 512, P, 256, 128, P, P, None, None) == ENULL           # qw without sw
+    assert f(P, P, P, None, 4, 512, P, 128, 128, P, None, None, None) == ESHAPE       # n % 256
+    assert f(P, P, P, None, 4, 500, P, 256, 128, P, None, None, None) == ESHAPE       # total_rows % 128
+    assert f(P, P, P, None, 4, 512, P, 256, 100, P, None, None, None) == ESHAPE       # k % 128
+    assert f(P, P, P, None, 4, 512, P + 2, 256, 128, P, None, None, None) == EALIGN   # w
+    assert f(P, P, P, None, 4, 512, P, 256, 128, P, P + 8, P, None) == EALIGN         # qw
+
+
 def test_wgrad_validation(raw):
     f = raw.fp8bs_gemm_wgrad
     assert f(P, P, P, P, 8, 8, 128, None, 8, 0, None) == ENULL

@@ -21,7 +21,7 @@ from oracle import (gemm_dgrad, gemm_fprop, gemm_wgrad, grouped_gemm, quantize_a
 from tests.gpu_util import (assert_gemm_parity, bf16_values_host, magnitude_codes, random_codes,
                             random_scales, to_dev, to_dev_bf16)
 from workloads import (config_by_name, device_expert_weights, gemm_inputs, grouped_inputs_host,
-                       wgrad_inputs)
+                       normal_bf16, wgrad_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -563,3 +563,88 @@ def test_wgrad_shape_sweep(gpu_lib, m, n, t):
     c64 = gemm_wgrad(qa[wr], sa[wr], qb[cols], sb[cols])
     mag = gemm_wgrad(magnitude_codes(qa[wr]), sa[wr], magnitude_codes(qb[cols]), sb[cols])
     assert_gemm_parity(got, c64, mag, out_bf16=False, label=f"wgrad sweep {m}x{n}x{t}")
+
+
+# ------------------------------------------------ grouped, bf16 weights -----
+
+def _special_weights(rng, num_e, n, k):
+    """bf16 expert weights N(0, 0.02) with special 128x128 blocks: all zero,
+    tiny (amax below 2^-64, with subnormals: the scaled coding path), and
+    large (|w| up to ~3e4)."""
+    w = normal_bf16(rng, (num_e, n, k), 0.02)
+    w[0, :128, :128] = 0
+    sign = rng.integers(0, 2, size=(128, 128)).astype(np.uint16) << 15
+    exp = rng.integers(0, 58, size=(128, 128)).astype(np.uint16)          # <= 2^-70 (0: subnormal)
+    w[num_e - 1, n - 128:, k - 128:] = sign | (exp << 7) | rng.integers(0, 128, size=(128, 128)).astype(np.uint16)
+    big = rng.integers(0x4500, 0x46F0, size=(128, 128)).astype(np.uint16)  # 2048 .. ~30000
+    w[num_e // 2, :128, k - 128:] = big | (rng.integers(0, 2, size=(128, 128)).astype(np.uint16) << 15)
+    return w
+
+
+def _routed_rows(counts):
+    """Padded segment starts and the row map (-1 on padding) for the counts."""
+    off = np.concatenate([[0], np.cumsum((np.asarray(counts) + 127) // 128 * 128)]).astype(np.int64)
+    rt = np.full(int(off[-1]), -1, np.int32)
+    for e, cnt in enumerate(counts):
+        rt[off[e]:off[e] + cnt] = np.arange(cnt, dtype=np.int32)
+    return off, rt
+
+
+@pytest.mark.parametrize("k", [128, 256, 384, 640, 896])
+def test_grouped_bf16w_equals_quantize_then_grouped(gpu_lib, k):
+    """The fused call (weights coded in the GEMM's copy waves) against
+    fp8bs_quantize_w_128x128 followed by fp8bs_grouped_gemm: C bit for bit,
+    with and without the row map; the stored codes and scales equal the block
+    quantizer's for every expert with rows and leave an expert without rows
+    untouched.  K = 128 .. 896 runs 1, 2, 3, 5 and 7 slab units (the copy
+    waves' schedule is unrolled by 6).  One expert's stored blocks (zero,
+    tiny and large ones) are also checked against the oracle."""
+    rng = np.random.default_rng(240 + k)
+    counts, n = [130, 0, 1, 256, 77], 256
+    num_e = len(counts)
+    off, rt = _routed_rows(counts)
+    rows = int(off[-1])
+    qa, sa = random_codes(rng, (rows, k)), random_scales(rng, (rows, k // 128))
+    pad = rt < 0
+    qa[pad], sa[pad] = 0, 0.0
+    w_h = _special_weights(rng, num_e, n, k)
+    w = to_dev_bf16(w_h)
+    qa_d, sa_d, seg, rt_d = to_dev(qa), to_dev(sa), to_dev(off.astype(np.int32)), to_dev(rt)
+    qw_ref, sw_ref = gpu_lib.fp8bs_quantize_w_128x128(w)
+    c_ref = gpu_lib.fp8bs_grouped_gemm(qa_d, sa_d, seg, qw_ref, sw_ref, row_token=rt_d)
+    qw = torch.full((num_e, n, k), 0x5A, dtype=torch.uint8, device="cuda")
+    sw = torch.full((num_e, n // 128, k // 128), -1.0, dtype=torch.float32, device="cuda")
+    c = gpu_lib.fp8bs_grouped_gemm_bf16w(qa_d, sa_d, seg, w, qw=qw, sw=sw, row_token=rt_d)
+    assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16)), f"k={k}: C with the row map"
+    c2 = gpu_lib.fp8bs_grouped_gemm_bf16w(qa_d, sa_d, seg, w)
+    assert torch.equal(c2.view(torch.int16), c_ref.view(torch.int16)), f"k={k}: C without the map"
+    for e, cnt in enumerate(counts):
+        if cnt:
+            assert torch.equal(qw[e], qw_ref[e]) and torch.equal(sw[e].view(torch.int32), sw_ref[e].view(torch.int32)), \
+                f"k={k}: stored weights of expert {e}"
+        else:
+            assert bool((qw[e] == 0x5A).all()) and bool((sw[e] == -1.0).all()), f"k={k}: expert {e} has no rows"
+    for e in (0, num_e - 1):
+        oq, os_ = quantize_w_128x128(w_h[e])
+        assert np.array_equal(qw[e].cpu().numpy(), oq) and np.array_equal(sw[e].cpu().numpy(), os_), f"oracle, expert {e}"
+
+
+def test_grouped_bf16w_c4_full_launch(gpu_lib):
+    """c4 at full size: the fused call against the two calls, whole outputs
+    bit for bit, and the stored weights of every expert with rows."""
+    cfg = config_by_name("c4")
+    g = grouped_inputs_host(cfg, with_weights=False)
+    off, counts = g["offsets"], g["counts"]
+    _, rt = _routed_rows(counts)
+    assert np.array_equal(_routed_rows(counts)[0], off)
+    w = device_expert_weights(cfg)
+    qa, sa = gpu_lib.fp8bs_quantize_act_1x128(to_dev_bf16(g["x"]))
+    seg, rt_d = to_dev(off.astype(np.int32)), to_dev(rt)
+    qw_ref, sw_ref = gpu_lib.fp8bs_quantize_w_128x128(w)
+    c_ref = gpu_lib.fp8bs_grouped_gemm(qa, sa, seg, qw_ref, sw_ref, row_token=rt_d)
+    qw, sw = torch.zeros_like(qw_ref), torch.zeros_like(sw_ref)
+    c = gpu_lib.fp8bs_grouped_gemm_bf16w(qa, sa, seg, w, qw=qw, sw=sw, row_token=rt_d)
+    assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16))
+    has = torch.from_numpy(np.asarray(counts) > 0).cuda()
+    assert torch.equal(qw[has], qw_ref[has]) and torch.equal(sw[has], sw_ref[has])
+    del w, qw_ref, qw
