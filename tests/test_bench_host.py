@@ -64,3 +64,36 @@ def test_traffic_lookup_rejects_stale_sources(monkeypatch, tmp_path):
     assert bench.load_traffic("c2:gemm_wgrad", "gemm") == 123
     assert bench.load_traffic("c2:quant_w", "quant") is None
     assert bench.load_traffic("c2:missing", "gemm") is None
+
+
+def test_call_roofline_picks_the_longer_bound():
+    """A call's bound is whichever of its FLOPs at the dense FP8 peak and its
+    algorithmic bytes at the HBM peak takes longer; `achieved` is that quantity
+    per second of the measured duration."""
+    # c4's fused grouped GEMM: 1.924 TFLOP over the routed rows, 23.23 GB moved
+    flops, nbytes = 2.0 * 32768 * 4096 * 7168, 23_234_300_416
+    c = bench.Call("gemm_grouped_bf16w", "gemm", None, flops=flops, nbytes=nbytes)
+    r = bench.call_roofline(c, 5.58e-3)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["algorithmic"] == nbytes
+    assert abs(r["achieved"] - nbytes / 5.58e-3 / 1e9) < 0.1
+    assert abs(r["frac"] - r["achieved"] / bench.HBM_PEAK_GBPS) < 1e-4
+    # a square layer GEMM: 2 * 4096^2 * 7168 FLOP over ~100 MB is MFMA-bound
+    c = bench.Call("gemm_fprop", "gemm", None, flops=2.0 * 4096 * 4096 * 7168, nbytes=100e6)
+    r = bench.call_roofline(c, 100e-6)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert abs(r["achieved"] - c.flops / 100e-6 / 1e12) < 0.1
+    # a quantizer has no FLOPs: always HBM
+    c = bench.Call("quant_w", "quant", None, nbytes=1e9)
+    assert bench.call_roofline(c, 1e-3)["bound"] == "hbm"
+
+
+def test_c4_two_calls_flag_parses():
+    sys_argv = sys.argv
+    try:
+        sys.argv = ["bench.py", "--c4-two-calls"]
+        a = bench.parse_args()
+        assert a.c4_two_calls and a.config == "c4" and a.steps == 20 and a.warmup == 5
+        sys.argv = ["bench.py"]
+        assert not bench.parse_args().c4_two_calls
+    finally:
+        sys.argv = sys_argv
