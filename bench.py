@@ -765,7 +765,7 @@ def main():
         ent.update(call_roofline(c, avg_s))
         if c.kind == "gemm":
             ent["frac_fp8_peak"] = round(c.flops / avg_s / 1e12 / FP8_PEAK_TFLOPS, 4)
-        elif copy_gbps:
+        if copy_gbps and ent["bound"] == "hbm":
             ent["frac_copy"] = round(c.nbytes / avg_s / 1e9 / copy_gbps, 4)
         ent["traffic"] = load_traffic(f"{args.config}:{c.name}", c.kind)
         return ent

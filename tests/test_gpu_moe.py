@@ -205,14 +205,15 @@ def test_combine_moe_workload_sampled(gpu_lib):
                    "4096 tokens x 7168, sampled tokens")
 
 
-@pytest.mark.parametrize("n", [128, 256])
-def test_dispatch_grouped_combine_chain(gpu_lib, n):
+@pytest.mark.parametrize("n,fused", [(128, False), (256, False), (256, True)])
+def test_dispatch_grouped_combine_chain(gpu_lib, n, fused):
     """Route -> payload -> grouped GEMM over the row capacity (with the route's row map) -> combine,
     against the oracle chain.
 
     The grouped GEMM runs over the capacity (no host read of the padded total):
     its rows past the padded total must stay untouched.  n = 128 runs the
-    128 x 128 grouped kernel, n = 256 the 128 x 256 warp-specialized one."""
+    128 x 128 grouped kernel, n = 256 the 128 x 256 warp-specialized one, and
+    fused the call that quantizes the bf16 expert weights itself."""
     cfg = dict(tokens=333, topk=6, experts=9, zipf_s=1.1, seed=21, K=512)
     d = moe_dispatch_inputs(cfg)
     k = 512
@@ -223,7 +224,10 @@ def test_dispatch_grouped_combine_chain(gpu_lib, n):
     qw, sw = gpu_lib.fp8bs_quantize_w_128x128(to_dev_bf16(w))
     cap = tok.numel()
     y = torch.full((cap, n), 77.0, dtype=torch.bfloat16, device="cuda")
-    gpu_lib.fp8bs_grouped_gemm(q, s, seg, qw, sw, c=y, row_token=tok)
+    if fused:                                  # weights coded inside the grouped GEMM
+        gpu_lib.fp8bs_grouped_gemm_bf16w(q, s, seg, to_dev_bf16(w), c=y, row_token=tok)
+    else:
+        gpu_lib.fp8bs_grouped_gemm(q, s, seg, qw, sw, c=y, row_token=tok)
     out = gpu_lib.fp8bs_moe_combine(y, slot, to_dev(d["gates"]))
     torch.cuda.synchronize()
     r = moe_route(d["ids"], 9)
