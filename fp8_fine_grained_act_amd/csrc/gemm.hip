@@ -64,7 +64,8 @@ struct GemmArgs {
   int64_t num_experts;
   int64_t tiles_m, tiles_n;
   int accumulate;
-  int64_t group_m;  // band height in m-tiles of the XCD-aware order; 0 = column-major, -1 = row-major
+  int64_t group_m;  // band height in m-tiles of the XCD-aware order; 0 = column-major, -1 = row-major,
+                    // -3 = grouped, experts' first m-tiles (tile_coords)
   float* ws;        // split contraction: FP32 partials [ksplit][m][n] (gridDim.y = ksplit)
   int64_t ksplit;
   int stream_out;   // bf16 output larger than half the last-level cache: non-temporal stores
@@ -122,6 +123,17 @@ __device__ inline TileMN tile_coords(const GemmArgs& p, uint32_t b) {
   if (p.group_m == -1) {            // row-major: all N tiles of one M tile in a row
     const uint32_t m = b / tiles_n;
     return TileMN{m, b - m * tiles_n};
+  }
+  if (p.group_m == -3) {
+    // grouped, each expert's first m-tile only: the XCDs step through the
+    // experts eight at a time, each running all N tiles of its expert, so the
+    // tile's rows of A are fetched into one L2.  An expert without rows (or
+    // past the last) gets the row past the last tile, which the kernel's
+    // end-of-rows check sends away.
+    const uint32_t j = b / kXcds;
+    const uint32_t e = kXcds * (j / tiles_n) + b % kXcds;
+    if (e >= (uint32_t)p.num_experts || p.seg[e] == p.seg[e + 1]) return TileMN{tiles_m, 0};
+    return TileMN{(uint32_t)p.seg[e] / 128u, j % tiles_n};
   }
   const uint32_t gm = (uint32_t)p.group_m;
   const uint32_t tiles = tiles_m * tiles_n;
@@ -1330,8 +1342,11 @@ template <bool W16 = false>
 static int launch_grouped_ws(GemmArgs a, hipStream_t s) {
   a.tiles_n = a.n / 256;
   a.tiles_m = a.m / 128;
-  a.group_m = -1;
-  const int64_t grid = a.tiles_m * a.tiles_n;
+  // the launch of only the experts' first m-tiles takes a grid of N tiles
+  // per expert (rounded up to whole steps of the eight XCDs)
+  a.group_m = a.tile_sel == 1 ? -3 : -1;
+  const int64_t grid = a.tile_sel == 1 ? (a.num_experts + kXcds - 1) / kXcds * kXcds * a.tiles_n
+                                       : a.tiles_m * a.tiles_n;
   if (grid > kMaxGrid) return FP8BS_ERR_SHAPE;
   // one tile per workgroup: the persistent form measured 9% slower here
   // (256 experts of 4096x7168), its in-loop store spilling registers
