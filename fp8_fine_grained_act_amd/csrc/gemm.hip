@@ -114,6 +114,10 @@ constexpr int kXcds = 8;
 struct TileMN {
   uint32_t m, n;
 };
+// The order of the experts' first m-tiles (-3) is compiled only into the
+// kernel that codes bf16 weights (ORDER), which calls this once per
+// workgroup; the other kernels compile as if it did not exist.
+template <int ORDER = 0>
 __device__ inline TileMN tile_coords(const GemmArgs& p, uint32_t b) {
   const uint32_t tiles_m = (uint32_t)p.tiles_m, tiles_n = (uint32_t)p.tiles_n;
   if (p.group_m == 0) {
@@ -124,7 +128,7 @@ __device__ inline TileMN tile_coords(const GemmArgs& p, uint32_t b) {
     const uint32_t m = b / tiles_n;
     return TileMN{m, b - m * tiles_n};
   }
-  if (p.group_m == -3) {
+  if (ORDER == -3 && p.group_m == -3) {
     // grouped, each expert's first m-tile only: the XCDs step through the
     // experts eight at a time, each running all N tiles of its expert, so the
     // tile's rows of A are fetched into one L2.  An expert without rows (or
@@ -840,8 +844,11 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   struct Origin {
     int64_t m0, n0;
   };
+  // grouped (one tile per workgroup): the tile is found once, here
+  TileMN grouped_tile{0, 0};
+  if constexpr (MODE == kGrouped) grouped_tile = tile_coords<W16 ? -3 : 0>(p, blockIdx.x);
   auto tile_origin = [&](int i) {
-    const TileMN t = tile_coords(p, (uint32_t)((int64_t)blockIdx.x + (int64_t)i * G));
+    const TileMN t = MODE == kGrouped ? grouped_tile : tile_coords(p, (uint32_t)((int64_t)blockIdx.x + (int64_t)i * G));
     return Origin{(int64_t)t.m * BM, (int64_t)t.n * BN};
   };
 
@@ -1344,6 +1351,7 @@ static int launch_grouped_ws(GemmArgs a, hipStream_t s) {
   a.tiles_m = a.m / 128;
   // the launch of only the experts' first m-tiles takes a grid of N tiles
   // per expert (rounded up to whole steps of the eight XCDs)
+  if (a.tile_sel == 1 && !W16) return FP8BS_ERR_SHAPE;   // the order is compiled into the bf16 kernel only
   a.group_m = a.tile_sel == 1 ? -3 : -1;
   const int64_t grid = a.tile_sel == 1 ? (a.num_experts + kXcds - 1) / kXcds * kXcds * a.tiles_n
                                        : a.tiles_m * a.tiles_n;
