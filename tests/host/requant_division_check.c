@@ -2,12 +2,13 @@
  * Host check of the reciprocal-and-correction quotient used by the re-tiling
  * kernel, whose numerators are arbitrary binary32 values (x_hat = fl32(s *
  * dec(q)) is not a bf16 value, so the exhaustive bf16 check does not cover it).
- * For a divisor s = fl32(amax/448) and a numerator 0 <= a <= amax:
- *   amax >= 2^-64:  d = s,          a' = a
- *   amax <  2^-64:  d = s * 2^64,   a' = a * 2^64   (both exact)
- *   r = fl32(1/d) (0 when d == 0), q0 = a'*r, e = fma(-q0, d, a'), q = fma(e, r, q0)
- * must give the same E4M3 code (nearest even, saturating) as the IEEE binary32
- * quotient a/s (0 when s == 0), and q must not exceed 464.  (This is
+ * For a divisor s = fl32(amax/448) and a signed numerator x, |x| <= amax:
+ *   amax >= 2^-64:  d = s,          x' = x
+ *   amax <  2^-64:  d = s * 2^64,   x' = x * 2^64   (both exact)
+ *   r = fl32(1/d) (0 when d == 0), q0 = x'*r, e = fma(q0, d, -x'), q = fma(-e, r, q0)
+ * must give the same E4M3 code (nearest even, saturating, sign bit from the
+ * sign of x, also for -0) as the IEEE binary32 quotient |x|/s (0 when s == 0)
+ * with x's sign, and |q| must not exceed 464.  (This is
  * Markstein's correction: with r the correctly rounded reciprocal and q0
  * within one ulp of the quotient, q is the correctly rounded quotient; the
  * scaling keeps e and r clear of underflow and overflow.)
@@ -49,21 +50,30 @@ static uint64_t next(void) { rng ^= rng << 13; rng ^= rng >> 7; rng ^= rng << 17
 
 static long long bad = 0, total = 0;
 
-static void check(float amax, float a) {
+/* signed code: the sign bit of v, then the code of |v| */
+static uint32_t e4m3_signed(float v) { return ((bits(v) >> 24) & 0x80u) | e4m3(fabsf(v)); }
+
+static void check1(float amax, float x) {
   const float s = amax / 448.0f;
   const int tiny = amax < 0x1p-64f;
   const float d = tiny ? s * 0x1p64f : s;
   const float r = d == 0.0f ? 0.0f : 1.0f / d;
-  const float ap = tiny ? a * 0x1p64f : a;
-  const float q0 = ap * r;
-  const float e = fmaf(-q0, d, ap);
-  const float q = fmaf(e, r, q0);
-  const float ref = s == 0.0f ? 0.0f : a / s;
+  const float xp = tiny ? x * 0x1p64f : x;
+  const float q0 = xp * r;
+  const float e = fmaf(q0, d, -xp);
+  const float q = fmaf(-e, r, q0);
+  const float ref = s == 0.0f ? copysignf(0.0f, x) : copysignf(fabsf(x) / s, x);
   ++total;
-  if (e4m3(q) != e4m3(ref) || q > 464.0f) {
-    if (bad < 8) printf("mismatch amax=%a a=%a q=%a ieee=%a\n", amax, a, q, ref);
+  if (e4m3_signed(q) != e4m3_signed(ref) || fabsf(q) > 464.0f) {
+    if (bad < 8) printf("mismatch amax=%a x=%a q=%a ieee=%a\n", amax, x, q, ref);
     ++bad;
   }
+}
+
+/* both signs of a magnitude 0 <= a <= amax */
+static void check(float amax, float a) {
+  check1(amax, a);
+  check1(amax, -a);
 }
 
 int main(int argc, char** argv) {
@@ -86,6 +96,7 @@ int main(int argc, char** argv) {
       if (amax == 0.0f) continue;
       const float s = amax / 448.0f;
       check(amax, amax);
+      check(amax, 0.0f);                           /* +0 and -0 */
       for (int i = 0; i < nb; ++i) {
         const float c = bound[i] * s;              /* near a rounding boundary of the quotient */
         if (!(c > 0.0f)) continue;
