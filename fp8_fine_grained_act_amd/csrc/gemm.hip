@@ -14,7 +14,8 @@
 //
 // Two kernels share the slab layout below: gemm_kernel (128 x 128 or 64 x 128
 // tiles, every wave both copies and multiplies, two workgroups per CU; small
-// and mid-size problems) and gemm_ws_kernel (256 x 128, 192 x 128, 128 x 192
+// problems, and the grouped GEMM whose n is not a multiple of 256) and
+// gemm_ws_kernel (256 x 128, 192 x 128, 128 x 192
 // and, for the MoE grouped GEMM, 128 x 256 tiles; separate copy and MFMA
 // waves; persistent over tiles where a workgroup gets several; described
 // above that kernel).  The host picks the kernel, tile shape and tile order
@@ -1368,22 +1369,29 @@ static int launch_grouped_ws(GemmArgs a, hipStream_t s) {
 using namespace fp8bs;
 
 // Kernel choice.  The warp-specialized kernel (gemm_ws_kernel) is the faster
-// one per CU, but it runs one large tile per CU; when a problem has fewer
-// 256 x 128 tiles than three quarters of the CUs, gemm_kernel (smaller tiles,
-// two workgroups per CU) keeps more of the chip busy.
-static bool use_ws(int64_t m, int64_t n) {
-  const int64_t tiles = ((m + 255) / 256) * ((n + 127) / 128);
-  return 4 * tiles >= 3 * cu_count();
+// one per CU, but it runs one large tile per CU; when a problem's 192 x 128
+// tiles would cover fewer than half the CUs (a quarter for the weight
+// gradient, whose long contraction gains more from the faster kernel than
+// it loses to idle CUs), gemm_kernel (smaller tiles, two workgroups per CU)
+// keeps more of the chip busy.  Counting 256 x 128 tiles against three
+// quarters of the CUs, as before the 192-row tiles existed, sent shapes the
+// warp-specialized kernel runs 18-41% faster to gemm_kernel (1536x3584 weight
+// gradient over 16384 tokens: 188 -> 110 us; forward 3072x1536x7168: 55.7 ->
+// 41.6 us); below a quarter (forward) it loses (768x2048x7168: 35.6 -> 38.9 us).
+static bool use_ws(int64_t m, int64_t n, bool wgrad) {
+  const int64_t tiles = ((m + 191) / 192) * ((n + 127) / 128);
+  return (wgrad ? 4 : 2) * tiles >= cu_count();
 }
 
 // Offsets inside one operand are 32-bit (buffer addressing): a tile's rows of
 // A or B, and the dgrad weight as a whole, must stay below 4 GiB.
 static bool fits_u32(int64_t bytes) { return bytes < 0xFFFFFFFFLL; }
 
-// gemm_kernel tiles: 128 x 128 (2 x 2 waves of 64 x 64, 2 stages) for
-// mid-size problems, and 64 x 128 (2 x 2 waves of 32 x 64, 3 stages) for
-// problems with fewer 128 x 128 tiles than CUs: the output 4096x512 over a
-// 32768-long contraction (128 tiles) measured 209 -> 168 us with them.
+// gemm_kernel tiles: 128 x 128 (2 x 2 waves of 64 x 64, 2 stages) for the
+// grouped GEMM whose n is not a multiple of 256, and 64 x 128 (2 x 2 waves of
+// 32 x 64, 3 stages) for problems too small for the warp-specialized kernel
+// (they have fewer 128 x 128 tiles than CUs: the output 4096x512 over a
+// 32768-long contraction, 128 tiles, measured 209 -> 168 us with them).
 #define FP8BS_TILE_MID 128, 128, 2, 2, 2
 #define FP8BS_TILE_SMALL 64, 128, 2, 2, 3
 // Split contraction for activation gradients with few output tiles and a long
@@ -1458,24 +1466,19 @@ static bool split_grid_ok(int64_t m, int64_t n, int64_t ks) {
   return tiles <= kMaxGrid && ks <= 65535 && (m * n / 4 + 255) / 256 <= kMaxGrid;
 }
 
-static bool small_tiles(int64_t m, int64_t n) {
-  return ((m + 127) / 128) * ((n + 127) / 128) < cu_count();
-}
-
 // fp8bs_gemm without a contraction split: the warp-specialized kernel for
-// problems with enough large tiles, else gemm_kernel's mid or small tiles.
+// problems with enough large tiles, else gemm_kernel's small tiles.  (A
+// problem that use_ws turns away has fewer 128 x 128 tiles than CUs, since
+// those are at most twice its 192 x 128 tiles, so gemm_kernel's 128 x 128
+// tiles serve only the grouped GEMM.)
 static int gemm_unsplit(GemmArgs a, int b_layout, hipStream_t stream) {
   const int64_t m = a.m, n = a.n;
-  if (use_ws(m, n)) {
+  if (use_ws(m, n, false)) {
     if (b_layout == 0) return launch_gemm_ws<kFprop>(a, stream, cu_count());
     return launch_gemm_ws<kDgrad>(a, stream, cu_count());
   }
-  if (small_tiles(m, n)) {
-    if (b_layout == 0) return launch_gemm<kFprop, FP8BS_TILE_SMALL>(a, stream);
-    return launch_gemm<kDgrad, FP8BS_TILE_SMALL>(a, stream);
-  }
-  if (b_layout == 0) return launch_gemm<kFprop, FP8BS_TILE_MID>(a, stream);
-  return launch_gemm<kDgrad, FP8BS_TILE_MID>(a, stream);
+  if (b_layout == 0) return launch_gemm<kFprop, FP8BS_TILE_SMALL>(a, stream);
+  return launch_gemm<kDgrad, FP8BS_TILE_SMALL>(a, stream);
 }
 
 // Argument checks of fp8bs_gemm; on success fills *a.
@@ -1625,7 +1628,6 @@ extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_
       ldc % 4)
     return FP8BS_ERR_ALIGN;
   GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, t, nullptr, 0, 0, 0, accumulate, 0};
-  if (use_ws(m, n)) return launch_gemm_ws<kWgrad>(a, (hipStream_t)stream, cu_count());
-  if (small_tiles(m, n)) return launch_gemm<kWgrad, FP8BS_TILE_SMALL>(a, (hipStream_t)stream);
-  return launch_gemm<kWgrad, FP8BS_TILE_MID>(a, (hipStream_t)stream);
+  if (use_ws(m, n, true)) return launch_gemm_ws<kWgrad>(a, (hipStream_t)stream, cu_count());
+  return launch_gemm<kWgrad, FP8BS_TILE_SMALL>(a, (hipStream_t)stream);
 }
