@@ -833,7 +833,7 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   const int nkb = (int)(K / BK);               // K blocks of a row (the width of the scale rows)
   // SPLIT: workgroup (x, y) runs slabs [y * nslab, (y + 1) * nslab) of tile x
   // and stores its FP32 partial to ws[y]; a second kernel sums the partials
-  static_assert(!SPLIT || (MODE == kDgrad && !PERSIST), "split contraction: plain dgrad tiles");
+  static_assert(!SPLIT || ((MODE == kDgrad || MODE == kFprop) && !PERSIST), "split contraction: plain tiles");
   const int nslab = SPLIT ? nkb / (int)p.ksplit : nkb;
   const int kb0 = SPLIT ? (int)blockIdx.y * nslab : 0;
   // PERSIST = false: one tile per workgroup (grid = tiles), with the tile
@@ -1394,9 +1394,10 @@ static bool fits_u32(int64_t bytes) { return bytes < 0xFFFFFFFFLL; }
 // 32768-long contraction, 128 tiles, measured 209 -> 168 us with them).
 #define FP8BS_TILE_MID 128, 128, 2, 2, 2
 #define FP8BS_TILE_SMALL 64, 128, 2, 2, 3
-// Split contraction for activation gradients with few output tiles and a long
-// contraction (dX [4096, 512] over 32768: 64 tiles of 256x128 leave three
-// quarters of the CUs idle).  ksplit workgroups per tile each run one
+// Split contraction for forward and activation-gradient GEMMs with few output
+// tiles and a long contraction (dX [4096, 512] over 32768: 64 tiles of
+// 256x128 leave three quarters of the CUs idle; the MLA latent projection
+// 4096x640x7168, 80 tiles).  ksplit workgroups per tile each run one
 // contiguous range of K slabs on the warp-specialized kernel and store an
 // FP32 partial; splitk_reduce_kernel sums the partials in split order and
 // rounds once to bf16.  fp8bs_gemm takes the partials from a stream-ordered
@@ -1425,10 +1426,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *reinterpret_cast<uint2*>(c + row * ldc + col) = o;
 }
 
-// Contraction split of a dgrad: 1 (none) unless 256x128 tiles would fill at
-// most half the CUs; then the largest power of two that keeps tiles x split
-// within the CUs, divides the K blocks and leaves each split 16 or more.
-static int64_t dgrad_ksplit(int64_t m, int64_t n, int64_t k, int cus) {
+// Contraction split: 1 (none) unless 256x128 tiles would fill at most half
+// the CUs; then the largest power of two that keeps tiles x split within the
+// CUs, divides the K blocks and leaves each split 16 or more.
+static int64_t gemm_ksplit(int64_t m, int64_t n, int64_t k, int cus) {
+  if (use_ws(m, n, false)) return 1;
   const int64_t tiles = ((m + 255) / 256) * (n / 128);
   const int64_t nkb = k / BK;
   int64_t ks = 1;
@@ -1436,13 +1438,14 @@ static int64_t dgrad_ksplit(int64_t m, int64_t n, int64_t k, int cus) {
   return ks;
 }
 
-static int64_t dgrad_split_bytes(int64_t m, int64_t n, int64_t ks) {
+static int64_t split_bytes(int64_t m, int64_t n, int64_t ks) {
   return ks * m * n * (int64_t)sizeof(float);
 }
 
-// Enqueue the split dgrad with its FP32 partials in `ws` (at least
-// dgrad_split_bytes(m, n, ks) bytes, not read before it is written).
-static int launch_dgrad_split(GemmArgs a, hipStream_t s, int64_t ks, float* ws) {
+// Enqueue the split GEMM (MODE: forward or dgrad) with its FP32 partials in
+// `ws` (at least split_bytes(m, n, ks) bytes, not read before it is written).
+template <int MODE>
+static int launch_split(GemmArgs a, hipStream_t s, int64_t ks, float* ws) {
   a.tiles_n = a.n / 128;
   a.tiles_m = (a.m + 255) / 256;
   a.group_m = choose_group_m(a, 256, 128, 2);
@@ -1450,7 +1453,7 @@ static int launch_dgrad_split(GemmArgs a, hipStream_t s, int64_t ks, float* ws) 
   a.ws = ws;
   const int64_t tiles = a.tiles_m * a.tiles_n;
   const int64_t groups = a.m * a.n / 4;
-  hipLaunchKernelGGL((gemm_ws_kernel<kDgrad, 8, 256, 128, false, true>), dim3((unsigned)tiles, (unsigned)ks),
+  hipLaunchKernelGGL((gemm_ws_kernel<MODE, 8, 256, 128, false, true>), dim3((unsigned)tiles, (unsigned)ks),
                      dim3(64 * 12), 0, s, a);
   int st = launch_status();
   if (st == FP8BS_OK) {
@@ -1502,26 +1505,25 @@ extern "C" int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb,
   const int chk = gemm_check(qa, sa, qb, sb, m, n, k, b_layout, c, ldc, &a);
   if (chk != FP8BS_OK) return chk;
   hipStream_t s = (hipStream_t)stream;
-  if (b_layout == 1) {
-    const int64_t ks = dgrad_ksplit(m, n, k, cu_count());
-    if (ks > 1) {
-      if (!split_grid_ok(m, n, ks)) return FP8BS_ERR_SHAPE;
-      void* ws = nullptr;
-      if (hipMallocAsync(&ws, (size_t)dgrad_split_bytes(m, n, ks), s) == hipSuccess) {
-        int st = launch_dgrad_split(a, s, ks, static_cast<float*>(ws));
-        if (hipFreeAsync(ws, s) != hipSuccess && st == FP8BS_OK) st = FP8BS_ERR_LAUNCH;
-        return st;
-      }
-      // no memory for the partials: clear the runtime's error state and run
-      // the unsplit kernels (same result within rounding, other bits)
-      (void)hipGetLastError();
+  const int64_t ks = gemm_ksplit(m, n, k, cu_count());
+  if (ks > 1) {
+    if (!split_grid_ok(m, n, ks)) return FP8BS_ERR_SHAPE;
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, (size_t)split_bytes(m, n, ks), s) == hipSuccess) {
+      int st = b_layout == 0 ? launch_split<kFprop>(a, s, ks, static_cast<float*>(ws))
+                             : launch_split<kDgrad>(a, s, ks, static_cast<float*>(ws));
+      if (hipFreeAsync(ws, s) != hipSuccess && st == FP8BS_OK) st = FP8BS_ERR_LAUNCH;
+      return st;
     }
+    // no memory for the partials: clear the runtime's error state and run
+    // the unsplit kernels (same result within rounding, other bits)
+    (void)hipGetLastError();
   }
   return gemm_unsplit(a, b_layout, s);
 }
 
 // ---- fp8bs_gemm without allocation -------------------------------------------
-// The split dgrad's FP32 partials live in one fixed device array per GPU.  A
+// The split GEMM's FP32 partials live in one fixed device array per GPU.  A
 // split is chosen only when tiles x split <= CUs, so its partials take at most
 // CUs x 256 x 128 floats: 32 MiB on the 256 CUs of an MI355X.  In host code
 // the array's name stands for no device address: kernels get the address that
@@ -1555,15 +1557,13 @@ extern "C" int fp8bs_gemm_noalloc(const uint8_t* qa, const float* sa, const uint
   const int chk = gemm_check(qa, sa, qb, sb, m, n, k, b_layout, c, ldc, &a);
   if (chk != FP8BS_OK) return chk;
   hipStream_t s = (hipStream_t)stream;
-  if (b_layout == 1) {
-    const int64_t ks = dgrad_ksplit(m, n, k, cu_count());
-    if (ks > 1) {
-      if (!split_grid_ok(m, n, ks)) return FP8BS_ERR_SHAPE;
-      if (dgrad_split_bytes(m, n, ks) > kScratchBytes) return FP8BS_ERR_SCRATCH;
-      float* ws = scratch_device_ptr();
-      if (ws == nullptr) return FP8BS_ERR_LAUNCH;
-      return launch_dgrad_split(a, s, ks, ws);
-    }
+  const int64_t ks = gemm_ksplit(m, n, k, cu_count());
+  if (ks > 1) {
+    if (!split_grid_ok(m, n, ks)) return FP8BS_ERR_SHAPE;
+    if (split_bytes(m, n, ks) > kScratchBytes) return FP8BS_ERR_SCRATCH;
+    float* ws = scratch_device_ptr();
+    if (ws == nullptr) return FP8BS_ERR_LAUNCH;
+    return b_layout == 0 ? launch_split<kFprop>(a, s, ks, ws) : launch_split<kDgrad>(a, s, ks, ws);
   }
   return gemm_unsplit(a, b_layout, s);
 }

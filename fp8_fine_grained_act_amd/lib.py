@@ -226,7 +226,7 @@ def fp8bs_gemm(qa, sa, qb, sb, b_layout=0, c=None, stream=None, _entry="fp8bs_ge
 
 
 def fp8bs_gemm_noalloc(qa, sa, qb, sb, b_layout=0, c=None, stream=None):
-    """fp8bs_gemm that never allocates device memory (the split dgrad uses the library's fixed array).
+    """fp8bs_gemm that never allocates device memory (a split contraction uses the library's fixed array).
     c is allocated here only when the caller passes none."""
     return fp8bs_gemm(qa, sa, qb, sb, b_layout=b_layout, c=c, stream=stream, _entry="fp8bs_gemm_noalloc")
 

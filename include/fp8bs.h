@@ -6,17 +6,17 @@
  * returns at once.  The caller owns every buffer it passes.
  *
  * Memory and state:
- *   - One path allocates: fp8bs_gemm with b_layout == 1, when it splits the
- *     contraction over workgroups, takes its FP32 partials from a
- *     stream-ordered allocation on the call's stream (hipMallocAsync, freed
- *     with hipFreeAsync after use).  If that allocation fails it clears the
- *     runtime's error and runs the unsplit kernels instead.
+ *   - One path allocates: fp8bs_gemm, when it splits the contraction over
+ *     workgroups, takes its FP32 partials from a stream-ordered allocation
+ *     on the call's stream (hipMallocAsync, freed with hipFreeAsync after
+ *     use).  If that allocation fails it clears the runtime's error and runs
+ *     the unsplit kernels instead.
  *     fp8bs_gemm_noalloc is the same call without allocation.
  *   - The library caches one value per device: its compute-unit count (an
  *     atomic per device ordinal, filled on first use).  Tile shapes and the
- *     contraction split are chosen from it, so the bits of a bf16 dgrad
- *     result can differ between devices with different CU counts (always
- *     within the same error bound).
+ *     contraction split are chosen from it, so the bits of a bf16 forward or
+ *     dgrad result can differ between devices with different CU counts
+ *     (always within the same error bound).
  *   - fp8bs_gemm_noalloc keeps its split partials in one fixed device array
  *     per GPU (see its declaration).
  *   Apart from that shared array, calls are re-entrant and thread-safe.
@@ -172,9 +172,10 @@ int fp8bs_quantize_w_128x128(const uint16_t* w, int64_t n, int64_t k, int64_t ld
  *   c   bf16 [m, n], row stride ldc elements
  *   m >= 1 (any), n % 128 == 0, k % 128 == 0.
  * Alignment: qa, qb, c 16-byte aligned; ldc % 8 == 0, ldc >= n.
- * Workspace (b_layout == 1 only): when the output's 256x128 tiles would fill
- * at most half the compute units and the contraction is long (at least 32
- * blocks), the contraction is split over workgroups.  Their FP32 partials,
+ * Workspace: when the output's 192x128 tiles would cover fewer than half the
+ * compute units (so its 256x128 tiles fill at most half of them) and the
+ * contraction is long (at least 32 blocks), the contraction is split over
+ * workgroups.  Their FP32 partials,
  * split x m x n x 4 bytes (split <= the compute-unit count / tiles, so at most
  * CUs x 128 KiB), take a stream-ordered allocation on `stream`
  * (hipMallocAsync, freed with hipFreeAsync after the summing kernel; graph
@@ -192,11 +193,11 @@ int fp8bs_gemm(const uint8_t* qa, const float* sa, const uint8_t* qb, const floa
  * graph capture that must record no allocation, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
  * fp8bs_gemm; it never allocates.  Where fp8bs_gemm would split the
- * contraction of a dgrad (b_layout == 1), the FP32 partials go to a fixed
+ * contraction (either b_layout), the FP32 partials go to a fixed
  * device array of 32 MiB per GPU, part of the library's code object and held
  * until the process ends; the split is chosen only when
  * split x tiles <= compute units, so on a 256-CU MI355X it always fits.
- * Every call on one GPU shares that array: calls whose split dgrads overlap in
+ * Every call on one GPU shares that array: calls whose splits overlap in
  * time on one GPU (other streams, other host threads) race and give wrong
  * results; order them on one stream.  Nothing in the array needs clearing (each
  * call writes the partials it reads).

@@ -517,6 +517,26 @@ def test_dgrad_split_contraction(gpu_lib):
                            label=f"dgrad split {mo}x{ko}x{kc}")
 
 
+def test_forward_split_contraction(gpu_lib):
+    """Forward GEMMs too small for the warp-specialized kernel (192x128 tiles for
+    fewer than half the CUs) with a long contraction split it like the dgrad:
+    ragged M, the MLA latent projection 4096x640x7168 (split 2), splits of 4,
+    a strided output whose padding columns keep their sentinel."""
+    rng = np.random.default_rng(242)
+    for m, n, k in [(1000, 256, 8192), (4096, 640, 7168), (4096, 512, 16384), (300, 512, 4096)]:
+        qa, sa = random_codes(rng, (m, k)), random_scales(rng, (m, k // 128))
+        qb, sb = random_codes(rng, (n, k)), random_scales(rng, (n // 128, k // 128))
+        big = torch.full((m, n + 64), -1, dtype=torch.int16, device="cuda")
+        gpu_lib.fp8bs_gemm(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), c=big.view(torch.bfloat16)[:, :n])
+        torch.cuda.synchronize()
+        assert bool((big[:, n:] == -1).all())
+        got = bf16_values_host(big.view(torch.bfloat16)[:, :n])
+        rows = _sample_rows(m, 96, seed=k) if m * k > 2 ** 26 else np.arange(m)
+        mag = gemm_fprop(magnitude_codes(qa[rows]), sa[rows], magnitude_codes(qb), sb)
+        assert_gemm_parity(got[rows], gemm_fprop(qa[rows], sa[rows], qb, sb), mag,
+                           label=f"fprop split {m}x{n}x{k}")
+
+
 # --------------------------------------------------------- random shape sweep -----
 
 def _sweep_shapes(seed, count):
