@@ -833,7 +833,7 @@ __global__ __launch_bounds__(64 * (MW + 4)) void gemm_ws_kernel(GemmArgs p) {
   const int nkb = (int)(K / BK);               // K blocks of a row (the width of the scale rows)
   // SPLIT: workgroup (x, y) runs slabs [y * nslab, (y + 1) * nslab) of tile x
   // and stores its FP32 partial to ws[y]; a second kernel sums the partials
-  static_assert(!SPLIT || ((MODE == kDgrad || MODE == kFprop) && !PERSIST), "split contraction: plain tiles");
+  static_assert(!SPLIT || (MODE != kGrouped && !PERSIST), "split contraction: plain tiles");
   const int nslab = SPLIT ? nkb / (int)p.ksplit : nkb;
   const int kb0 = SPLIT ? (int)blockIdx.y * nslab : 0;
   // PERSIST = false: one tile per workgroup (grid = tiles), with the tile
@@ -1426,6 +1426,35 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *reinterpret_cast<uint2*>(c + row * ldc + col) = o;
 }
 
+// The weight gradient's summing kernel: f32 out, c = sum (or c + sum with
+// accumulate), the partials added in split order first.
+__global__ __launch_bounds__(256) void splitk_reduce_f32_kernel(const float* __restrict__ ws, int64_t ksplit,
+                                                                int64_t m, int64_t n, float* __restrict__ c,
+                                                                int64_t ldc, int accumulate) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one 4-column group per thread
+  const int64_t qpr = n / 4;
+  if (q >= m * qpr) return;
+  const int64_t row = q / qpr, col = (q - row * qpr) * 4;
+  const int64_t plane = m * n;
+  float4 acc = *reinterpret_cast<const float4*>(ws + row * n + col);
+  for (int64_t k = 1; k < ksplit; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(ws + k * plane + row * n + col);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  float* dst = c + row * ldc + col;
+  if (accumulate) {
+    const float4 old = *reinterpret_cast<const float4*>(dst);
+    acc.x += old.x;
+    acc.y += old.y;
+    acc.z += old.z;
+    acc.w += old.w;
+  }
+  *reinterpret_cast<float4*>(dst) = acc;
+}
+
 // Contraction split: 1 (none) unless 256x128 tiles would fill at most half
 // the CUs; then the largest power of two that keeps tiles x split within the
 // CUs, divides the K blocks and leaves each split 16 or more.
@@ -1617,6 +1646,41 @@ extern "C" int fp8bs_grouped_gemm_bf16w(const uint8_t* qa, const float* sa, cons
   return launch_grouped_ws<false>(b, (hipStream_t)stream);
 }
 
+// Contraction (token) split of a weight gradient whose output tiles fill at
+// most half the CUs: 1 (none) otherwise; then the largest power of two that
+// keeps tiles x split within the CUs, divides the token blocks and leaves each
+// split 16 or more.  Tiles of 256 or 192 rows, whichever pads m less.
+static int64_t wgrad_ksplit(int64_t m, int64_t n, int64_t t, int cus, bool* tall) {
+  *tall = (m + 255) / 256 * 256 - m <= (m + 191) / 192 * 192 - m;
+  const int64_t tiles = (*tall ? (m + 255) / 256 : (m + 191) / 192) * ((n + 127) / 128);
+  const int64_t nkb = t / BK;
+  int64_t ks = 1;
+  while (2 * ks * tiles <= cus && nkb % (2 * ks) == 0 && nkb / (2 * ks) >= 16) ks *= 2;
+  return ks;
+}
+
+// Enqueue the split weight gradient with its FP32 partials in `ws` (at least
+// split_bytes(m, n, ks) bytes, not read before it is written).
+template <int BM>
+static int launch_wgrad_split(GemmArgs a, hipStream_t s, int64_t ks, float* ws) {
+  a.tiles_n = (a.n + 127) / 128;
+  a.tiles_m = (a.m + BM - 1) / BM;
+  a.group_m = choose_group_m(a, BM, 128, 4);
+  a.ksplit = ks;
+  a.ws = ws;
+  const int64_t tiles = a.tiles_m * a.tiles_n;
+  const int64_t groups = a.m * a.n / 4;
+  hipLaunchKernelGGL((gemm_ws_kernel<kWgrad, 4, BM, 128, false, true>), dim3((unsigned)tiles, (unsigned)ks),
+                     dim3(64 * 8), 0, s, a);
+  int st = launch_status();
+  if (st == FP8BS_OK) {
+    hipLaunchKernelGGL(splitk_reduce_f32_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, a.ws, ks,
+                       a.m, a.n, static_cast<float*>(a.c), a.ldc, a.accumulate);
+    st = launch_status();
+  }
+  return st;
+}
+
 extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
                                 int64_t m, int64_t n, int64_t t, float* c, int64_t ldc, int accumulate,
                                 void* stream) {
@@ -1628,6 +1692,22 @@ extern "C" int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_
       ldc % 4)
     return FP8BS_ERR_ALIGN;
   GemmArgs a{qa, sa, qb, sb, c, ldc, m, n, t, nullptr, 0, 0, 0, accumulate, 0};
-  if (use_ws(m, n, true)) return launch_gemm_ws<kWgrad>(a, (hipStream_t)stream, cu_count());
-  return launch_gemm<kWgrad, FP8BS_TILE_SMALL>(a, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  bool tall = false;
+  const int64_t ks = wgrad_ksplit(m, n, t, cu_count(), &tall);
+  if (ks > 1) {
+    if (m * n / 4 / 256 + 1 > kMaxGrid) return FP8BS_ERR_SHAPE;
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, (size_t)split_bytes(m, n, ks), s) == hipSuccess) {
+      int st = tall ? launch_wgrad_split<256>(a, s, ks, static_cast<float*>(ws))
+                    : launch_wgrad_split<192>(a, s, ks, static_cast<float*>(ws));
+      if (hipFreeAsync(ws, s) != hipSuccess && st == FP8BS_OK) st = FP8BS_ERR_LAUNCH;
+      return st;
+    }
+    // no memory for the partials: clear the runtime's error state and run
+    // the unsplit kernels (same result within rounding, other bits)
+    (void)hipGetLastError();
+  }
+  if (use_ws(m, n, true)) return launch_gemm_ws<kWgrad>(a, s, cu_count());
+  return launch_gemm<kWgrad, FP8BS_TILE_SMALL>(a, s);
 }

@@ -6,17 +6,17 @@
  * returns at once.  The caller owns every buffer it passes.
  *
  * Memory and state:
- *   - One path allocates: fp8bs_gemm, when it splits the contraction over
- *     workgroups, takes its FP32 partials from a stream-ordered allocation
- *     on the call's stream (hipMallocAsync, freed with hipFreeAsync after
- *     use).  If that allocation fails it clears the runtime's error and runs
- *     the unsplit kernels instead.
- *     fp8bs_gemm_noalloc is the same call without allocation.
+ *   - Two calls allocate: fp8bs_gemm and fp8bs_gemm_wgrad, when they split
+ *     the contraction over workgroups, take their FP32 partials from a
+ *     stream-ordered allocation on the call's stream (hipMallocAsync, freed
+ *     with hipFreeAsync after use).  If that allocation fails they clear the
+ *     runtime's error and run the unsplit kernels instead.
+ *     fp8bs_gemm_noalloc is fp8bs_gemm without allocation.
  *   - The library caches one value per device: its compute-unit count (an
  *     atomic per device ordinal, filled on first use).  Tile shapes and the
- *     contraction split are chosen from it, so the bits of a bf16 forward or
- *     dgrad result can differ between devices with different CU counts
- *     (always within the same error bound).
+ *     contraction split are chosen from it, so the bits of a GEMM result can
+ *     differ between devices with different CU counts (always within the
+ *     same error bound).
  *   - fp8bs_gemm_noalloc keeps its split partials in one fixed device array
  *     per GPU (see its declaration).
  *   Apart from that shared array, calls are re-entrant and thread-safe.
@@ -285,6 +285,15 @@ int fp8bs_grouped_gemm_bf16w(const uint8_t* qa, const float* sa, const int32_t* 
  *   accumulate == 0 overwrites c, == 1 adds to it (gradient accumulation).
  *   t % 128 == 0, m >= 1, n >= 1 with n % 4 == 0.
  * Alignment: qa, qb, c 16-byte aligned; ldc % 4 == 0, ldc >= n.
+ * Workspace: when the output's tiles (256 or 192 rows by 128 columns) fill at
+ * most half the compute units and there are at least 32 token blocks, the
+ * token contraction is split over workgroups.  Their FP32 partials, split x
+ * m x n x 4 bytes (at most CUs x 128 KiB), take a stream-ordered allocation on
+ * `stream` (hipMallocAsync, freed with hipFreeAsync after the summing kernel).
+ * The partials are summed in split order, then added to c when accumulating:
+ * deterministic for a given device and split, not bit-identical to an
+ * unsplit run.  If the allocation fails, the runtime's error is cleared and
+ * the unsplit kernels run instead (same error bound).
  */
 int fp8bs_gemm_wgrad(const uint8_t* qa, const float* sa, const uint8_t* qb, const float* sb,
                      int64_t m, int64_t n, int64_t t, float* c, int64_t ldc, int accumulate,

@@ -306,6 +306,44 @@ def test_wgrad_random_codes_ragged_and_accumulate(gpu_lib):
         assert_gemm_parity(c.cpu().numpy(), 2 * c64, 2 * mag, out_bf16=False, label="wgrad accumulate")
 
 
+def test_wgrad_split_contraction(gpu_lib):
+    """Weight gradients whose output tiles fill at most half the CUs and whose token
+    contraction is long split it (FP32 partials summed in split order, then added
+    to C with accumulate): ragged M and N, splits of 2 to 4, overwrite then
+    accumulate into a strided output whose padding columns keep their sentinel."""
+    rng = np.random.default_rng(243)
+    for m, n, t in [(300, 1000, 8192), (512, 2048, 4096), (256, 7168, 16384)]:
+        qa, qb = random_codes(rng, (m, t)), random_codes(rng, (n, t))
+        sa, sb = random_scales(rng, (m, t // 128)), random_scales(rng, (n, t // 128))
+        args = (to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb))
+        big = torch.full((m, n + 8), -7.0, dtype=torch.float32, device="cuda")
+        gpu_lib.fp8bs_gemm_wgrad(*args, c=big[:, :n])
+        torch.cuda.synchronize()
+        assert bool((big[:, n:] == -7.0).all())
+        rows = _sample_rows(m, 48, seed=t) if m * n * t > 2 ** 33 else np.arange(m)
+        c64 = gemm_wgrad(qa[rows], sa[rows], qb, sb)
+        mag = gemm_wgrad(magnitude_codes(qa[rows]), sa[rows], magnitude_codes(qb), sb)
+        assert_gemm_parity(big[:, :n].cpu().numpy()[rows], c64, mag, out_bf16=False, label=f"wgrad split {m}x{n}x{t}")
+        gpu_lib.fp8bs_gemm_wgrad(*args, c=big[:, :n], accumulate=1)
+        torch.cuda.synchronize()
+        assert bool((big[:, n:] == -7.0).all())
+        assert_gemm_parity(big[:, :n].cpu().numpy()[rows], 2 * c64, 2 * mag, out_bf16=False,
+                           label=f"wgrad split accumulate {m}x{n}x{t}")
+
+
+def test_wgrad_split_is_deterministic(gpu_lib):
+    """The split's partials are summed in a fixed order: two runs agree bit for bit."""
+    rng = np.random.default_rng(244)
+    m, n, t = 384, 1536, 16384
+    qa, qb = random_codes(rng, (m, t)), random_codes(rng, (n, t))
+    sa, sb = random_scales(rng, (m, t // 128)), random_scales(rng, (n, t // 128))
+    args = (to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb))
+    c1 = gpu_lib.fp8bs_gemm_wgrad(*args)
+    c2 = gpu_lib.fp8bs_gemm_wgrad(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
+
+
 def test_wgrad_c5_sampled_block(gpu_lib):
     """Full-size launch; the oracle checks sampled rows x sampled columns of dW.
 
