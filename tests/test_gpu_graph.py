@@ -1,8 +1,8 @@
 """HIP-graph capture of a whole training pass of a linear layer.
 
 The library's calls are plain kernel launches on the caller's stream (no
-memset, no host synchronisation; the one allocation, the split-contraction
-dgrad's workspace, is stream-ordered and recorded by the capture), so a
+memset, no host synchronisation; the one allocation, a split contraction's
+workspace, is stream-ordered and recorded by the capture), so a
 captured pass must replay to exactly the eager result.  The graph is replayed several times with
 unrelated eager work and synchronisations between the replays; every replay
 is compared bit for bit with the eager launches, and the eager result itself
@@ -183,3 +183,52 @@ def test_split_contraction_dgrad_graph_replays_match_eager(gpu_lib):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(_bits(out), ref), f"replay {rep} differs from the eager result"
+
+
+def test_split_forward_and_wgrad_graph_replays_match_eager(gpu_lib):
+    """The forward and the weight gradient split their contraction the same way
+    (a stream-ordered workspace for the FP32 partials; the weight gradient's
+    summing kernel adds into C when accumulating).  Captured together, with the
+    weight gradient accumulating into a buffer reset before every replay, the
+    replays reproduce the eager bits."""
+    rng = np.random.default_rng(252)
+    m, n, k = 1000, 256, 8192                          # forward: 8 tiles, split 4
+    mw, nw, t = 512, 2048, 4096                        # wgrad: 32 tiles, split 2
+    dev = lambda a: torch.from_numpy(a).cuda()        # noqa: E731
+    qa = dev(rng.integers(0, 0x7E, (m, k), dtype=np.uint8))
+    sa = dev(rng.uniform(0.5, 2.0, (m, k // 128)).astype(np.float32))
+    qb = dev(rng.integers(0, 0x7E, (n, k), dtype=np.uint8))
+    sb = dev(rng.uniform(0.5, 2.0, (n // 128, k // 128)).astype(np.float32))
+    qg = dev(rng.integers(0, 0x7E, (mw, t), dtype=np.uint8))
+    sg = dev(rng.uniform(0.5, 2.0, (mw, t // 128)).astype(np.float32))
+    qx = dev(rng.integers(0, 0x7E, (nw, t), dtype=np.uint8))
+    sx = dev(rng.uniform(0.5, 2.0, (nw, t // 128)).astype(np.float32))
+    base = dev(rng.standard_normal((mw, nw)).astype(np.float32))
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    dw = base.clone()
+
+    def calls():
+        gpu_lib.fp8bs_gemm(qa, sa, qb, sb, c=y)
+        gpu_lib.fp8bs_gemm_wgrad(qg, sg, qx, sx, c=dw, accumulate=1)
+
+    calls()
+    torch.cuda.synchronize()
+    ref_y, ref_dw = _bits(y).clone(), _bits(dw).clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y.view(torch.int16).fill_(-1)
+        dw.copy_(base)
+        gpu_lib.fp8bs_gemm_wgrad(qg, sg, qx, sx)          # unrelated eager work of the same kind
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(y), ref_y), f"replay {rep}: forward differs from the eager result"
+        assert torch.equal(_bits(dw), ref_dw), f"replay {rep}: weight gradient differs from the eager result"
