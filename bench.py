@@ -89,6 +89,10 @@ def parse_args():
     p.add_argument("--c4-two-calls", action="store_true",
                    help="c4: quantize the expert weights and run the grouped GEMM as two calls instead of the "
                         "grouped GEMM that quantizes its bf16 weights itself")
+    p.add_argument("--c4-keep-codes", action="store_true",
+                   help="c4: the fused grouped GEMM also stores the FP8 codes and scales of every expert "
+                        "(kept for later GEMMs such as a backward's dgrad), not only those its own tiles "
+                        "read back")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 512 MiB device-to-device copies (reference for HBM byte counters)")
     a = p.parse_args()
@@ -233,16 +237,18 @@ def build_layer_step(lib, cfg_name, rotate, dual=True, act_cache=False):
     return calls, state, desc, dict(d, kind="layer", cfg=cfg), []
 
 
-def build_grouped_step(lib, rotate, fused=True):
+def build_grouped_step(lib, rotate, fused=True, keep_codes=False):
     """Calls of configuration c4: the MoE expert grouped GEMM with its quantization.
 
     The step: quantize X (1x128 tiles over the padded expert-major rows; the
     padding rows are +0.0) -> quantize every expert's weight (128x128 blocks,
     codes and scales stored) -> grouped GEMM over the padded total.  By
     default the last two are one call, fp8bs_grouped_gemm_bf16w, whose copy
-    waves code each weight block where the GEMM reads it and store the codes
-    once per expert; with fused=False they are fp8bs_quantize_w_128x128 and
-    fp8bs_grouped_gemm (the same bits).  The MoE routing layout, the
+    waves code each weight block where the GEMM reads it; it stores the codes
+    of the experts with several 128-row tiles once, for their other tiles to
+    read back (keep_codes: those of every expert, for later GEMMs); with
+    fused=False they are fp8bs_quantize_w_128x128 and fp8bs_grouped_gemm
+    (the same bits).  The MoE routing layout, the
     dispatch payload (permute + 1x128 quantize from token order) and the
     combine (gate-weighted sum of each token's k expert rows, [capacity, 7168]
     bf16 expert outputs drawn once on the device) are returned as extra calls:
@@ -281,18 +287,22 @@ def build_grouped_step(lib, rotate, fused=True):
     x_bytes = total * k * 3 + total * kb * 4
     w_bytes = num_e * n * k * 3 + num_e * (n // 128) * kb * 4
     gemm_bytes = pairs * (k + kb * 4) + total * 4 + num_e * (n * k + (n // 128) * kb * 4) + total * n * 2
-    # fused: the bf16 weights read once, their codes and scales written once,
-    # the routed rows of X and the row map read, every padded output row written
-    fused_bytes = (num_e * n * k * 2 + num_e * n * k + num_e * (n // 128) * kb * 4 + pairs * (k + kb * 4)
-                   + total * 4 + total * n * 2)
+    # fused: the bf16 weights read once, the routed rows of X and the row map
+    # read, every padded output row written; with keep_codes also every
+    # expert's codes and scales written once (outputs of the call).  Without
+    # it the codes stored for the experts' other tiles are the call's own
+    # workspace and are not counted.
+    fused_bytes = (num_e * n * k * 2 + pairs * (k + kb * 4) + total * 4 + total * n * 2
+                   + (num_e * n * k + num_e * (n // 128) * kb * 4 if keep_codes else 0))
     quant_x = Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, q=qx, scales=sx),
                    nbytes=x_bytes, outs=(qx, sx))
     if fused:
         calls = [
             quant_x,
             Call("gemm_grouped_bf16w", "gemm",
-                 lambda: lib.fp8bs_grouped_gemm_bf16w(qx, sx, seg_pad, w, c=y, qw=qw, sw=sw, row_token=row_token),
-                 flops=2.0 * pairs * n * k, nbytes=fused_bytes, outs=(y, qw, sw)),
+                 lambda: lib.fp8bs_grouped_gemm_bf16w(qx, sx, seg_pad, w, c=y, qw=qw, sw=sw, row_token=row_token,
+                                                      keep_codes=keep_codes),
+                 flops=2.0 * pairs * n * k, nbytes=fused_bytes, outs=(y, qw, sw) if keep_codes else (y,)),
         ]
     else:
         calls = [
@@ -328,15 +338,22 @@ def build_grouped_step(lib, rotate, fused=True):
         Call("moe_combine", "moe", lambda: lib.fp8bs_moe_combine(y_down, slot, gates, out=out),
              nbytes=pairs * k * 2 + tokens * topk * 8 + tokens * k * 2, outs=(out,)),
     ]
-    step = ("1x128 quantization of the padded rows + grouped GEMM from the bf16 expert weights, each 128x128 "
-            "weight block quantized in the GEMM and its codes and scales stored once per expert" if fused else
-            "1x128 quantization of the padded rows + 128x128 quantization of all 256 expert weights + grouped GEMM")
+    if not fused:
+        step = "1x128 quantization of the padded rows + 128x128 quantization of all 256 expert weights + grouped GEMM"
+    elif keep_codes:
+        step = ("1x128 quantization of the padded rows + grouped GEMM from the bf16 expert weights, each 128x128 "
+                "weight block quantized in the GEMM and its codes and scales stored once per expert")
+    else:
+        step = ("1x128 quantization of the padded rows + grouped GEMM from the bf16 expert weights, each 128x128 "
+                "weight block quantized in the GEMM (codes stored once only for the experts with several "
+                "128-row tiles, which read them back)")
     desc = dict(workload="c4: MoE expert grouped GEMM, 4096 tokens x top-8 of 256 experts (Zipf 1.1 counts, "
                          "rows padded to 128 per expert), fused gate+up N=4096, K=7168; step = " + step,
                 routed_rows=pairs, padded_rows=total, experts=num_e, N=n, K=k,
                 value_flops="grouped GEMM over the routed rows, 2*32768*4096*7168",
                 bytes_counted="X quantizer: padded rows; grouped GEMM: routed rows of X, padded output rows"
-                              + ("; bf16 weights read once, codes written once" if fused else ""))
+                              + (("; bf16 weights read once" + (", codes written once" if keep_codes else ""))
+                                 if fused else ""))
     data = dict(kind="c4", x=host["x"], counts=counts, offsets=offsets, w_dev=w, cfg=cfg)
     return calls, state, desc, data, extras
 
@@ -700,7 +717,8 @@ def main():
         calls, state, desc, data, extras = build_layer_step(lib, args.config, args.rotate,
                                                             dual=not args.separate_quant, act_cache=args.act_cache)
     elif args.config == "c4":
-        calls, state, desc, data, extras = build_grouped_step(lib, args.rotate, fused=not args.c4_two_calls)
+        calls, state, desc, data, extras = build_grouped_step(lib, args.rotate, fused=not args.c4_two_calls,
+                                                              keep_codes=args.c4_keep_codes)
     else:
         calls, state, desc, data, extras = build_wgrad_step(lib, args.rotate, act_cache=args.act_cache)
     if args.act_cache:

@@ -75,6 +75,8 @@ struct GemmArgs {
   uint8_t* qw;               // and their codes / scales written once per expert, or null
   float* sw;
   int tile_sel;              // grouped: 0 every tile, 1 only each expert's first m-tile, 2 the others
+  int keep_all;              // grouped from bf16 weights with qw: 1 every expert's codes stored, 0 only
+                             // those of experts with several m-tiles (the ones read back)
 };
 
 // Expert whose segment holds row m0: the largest e with seg[e] <= m0 (empty
@@ -601,9 +603,11 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // v + 2 loads.  One barrier more than the FP8 path, before barrier 0, lets
 // the maxima of unit 0 cross; the MFMA waves pass it too.
 //
-// The expert's first tile (the one at its segment start) also stores the
-// codes and block scales to qw / sw, so the weights of every expert with rows
-// are coded once in memory for the GEMMs that follow (the backward's dgrad).
+// With qw / sw, the expert's first tile (the one at its segment start) also
+// stores the codes and block scales there: those of every expert with rows
+// (keep_all, codes kept for the GEMMs that follow, such as a backward's
+// dgrad), or only those of experts with several m-tiles, whose other m-tiles
+// read them back in the call's second launch.
 // ---------------------------------------------------------------------------
 template <int BM, int BN>
 __device__ __forceinline__ void copy_waves_bf16_weights(const GemmArgs& p, int c, int lane, int units,
@@ -630,7 +634,8 @@ __device__ __forceinline__ void copy_waves_bf16_weights(const GemmArgs& p, int c
   const int wrow = 64 * c + (lane >> 4);       // the lane's first weight row in the tile
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w16 + ((int64_t)e * N + n0) * K, (int64_t)BN * K * 2);
   const uint32_t voff_w = (uint32_t)((wrow * K + 8 * j) * 2);
-  const bool store_q = p.qw != nullptr && m0 == (int64_t)p.seg[e];
+  const bool store_q = p.qw != nullptr && m0 == (int64_t)p.seg[e] &&
+                       (p.keep_all || (int64_t)p.seg[e + 1] - m0 > BM);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qw + ((int64_t)e * N + n0) * K, store_q ? (int64_t)BN * K : 0);
   const uint32_t voff_q = (uint32_t)(wrow * K + 8 * j);
 
@@ -1618,8 +1623,10 @@ extern "C" int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int3
 extern "C" int fp8bs_grouped_gemm_bf16w(const uint8_t* qa, const float* sa, const int32_t* seg_offsets,
                                         const int32_t* row_token, int64_t num_experts, int64_t total_rows,
                                         const uint16_t* w, int64_t n, int64_t k, uint16_t* c, uint8_t* qw,
-                                        float* sw, void* stream) {
+                                        float* sw, int keep_codes, void* stream) {
   if (!qa || !sa || !seg_offsets || !w || !c || (qw == nullptr) != (sw == nullptr)) return FP8BS_ERR_NULL;
+  if (keep_codes != 0 && keep_codes != 1) return FP8BS_ERR_FLAG;
+  if (keep_codes && !qw) return FP8BS_ERR_NULL;
   if (num_experts < 1 || num_experts > 65536 || total_rows <= 0 || total_rows % 128 || n <= 0 ||
       k <= 0 || n % 256 || k % BK)
     return FP8BS_ERR_SHAPE;
@@ -1628,11 +1635,12 @@ extern "C" int fp8bs_grouped_gemm_bf16w(const uint8_t* qa, const float* sa, cons
       !aligned(sw, 4) || !aligned(seg_offsets, 4) || !aligned(row_token, 4))
     return FP8BS_ERR_ALIGN;
   GemmArgs a{qa, sa, nullptr, nullptr, c, n, total_rows, n, k, seg_offsets, num_experts, 0, 0, 0, 0, nullptr, 1,
-             total_rows * n * 2 > kStreamBytes, row_token, w, qw, sw, 0};
+             total_rows * n * 2 > kStreamBytes, row_token, w, qw, sw, 0, keep_codes};
   if (!qw) return launch_grouped_ws<true>(a, (hipStream_t)stream);
-  // With the codes stored: each expert's first m-tile codes the expert's
-  // weights from bf16 (each weight read once) and stores them; then the
-  // expert's other m-tiles read the stored codes, as fp8bs_grouped_gemm would.
+  // With qw / sw: each expert's first m-tile codes the expert's weights from
+  // bf16 (each weight read once) and stores them (all experts, or only those
+  // with several m-tiles); then the expert's other m-tiles read the stored
+  // codes, as fp8bs_grouped_gemm would.
   a.tile_sel = 1;
   const int st = launch_grouped_ws<true>(a, (hipStream_t)stream);
   if (st != FP8BS_OK) return st;

@@ -33,7 +33,7 @@ _SIGNATURES = {
     "fp8bs_grouped_gemm": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64,
                            _i64, _c_void_p, _c_void_p],
     "fp8bs_grouped_gemm_bf16w": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _i64, _i64,
-                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+                                 _c_void_p, _c_void_p, _c_void_p, _int, _c_void_p],
     "fp8bs_gemm_wgrad": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _int,
                          _c_void_p],
     "fp8bs_moe_route": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p],
@@ -267,12 +267,17 @@ def fp8bs_grouped_gemm(qa, sa, seg_offsets, qb, sb, c=None, stream=None, row_tok
     return c
 
 
-def fp8bs_grouped_gemm_bf16w(qa, sa, seg_offsets, w, c=None, qw=None, sw=None, stream=None, row_token=None):
+def fp8bs_grouped_gemm_bf16w(qa, sa, seg_offsets, w, c=None, qw=None, sw=None, stream=None, row_token=None,
+                             keep_codes=None):
     """MoE grouped GEMM from bf16 expert weights w [E, n, k]: bf16 C [R, n], the same bits as
     fp8bs_grouped_gemm over fp8bs_quantize_w_128x128(w).
 
-    qw (uint8 [E, n, k]) and sw (float32 [E, n/128, k/128]), both or neither: when given, the
-    weight codes and scales of every expert that owns rows are stored there."""
+    qw (uint8 [E, n, k]) and sw (float32 [E, n/128, k/128]), both or neither.  keep_codes
+    (default: True when they are given) stores the weight codes and scales of every expert
+    that owns rows there; keep_codes=False uses them as a workspace, storing only the codes
+    of experts with more than one 128-row tile (read back by those tiles)."""
+    if keep_codes is None:
+        keep_codes = qw is not None
     _dev(qa, torch.uint8, "qa")
     _dev(sa, torch.float32, "sa")
     _dev(w, torch.bfloat16, "w")
@@ -308,7 +313,8 @@ def fp8bs_grouped_gemm_bf16w(qa, sa, seg_offsets, w, c=None, qw=None, sw=None, s
     st = raw.fp8bs_grouped_gemm_bf16w(qa.data_ptr(), sa.data_ptr(), seg_offsets.data_ptr(),
                                       None if row_token is None else row_token.data_ptr(), num_e, rows,
                                       w.data_ptr(), n, k, c.data_ptr(), None if qw is None else qw.data_ptr(),
-                                      None if sw is None else sw.data_ptr(), _stream(stream))
+                                      None if sw is None else sw.data_ptr(), 1 if keep_codes else 0,
+                                      _stream(stream))
     _check("fp8bs_grouped_gemm_bf16w", st)
     return c
 

@@ -255,21 +255,29 @@ int fp8bs_grouped_gemm(const uint8_t* qa, const float* sa, const int32_t* seg_of
  * reads it, so the FP8 weights are not read back from memory.
  *   w    bf16 [num_experts, n, k] contiguous
  *   qw   E4M3 [num_experts, n, k] and sw f32 [num_experts, n/128, k/128], or
- *        both NULL: the codes and scales of every expert that owns at least
- *        one row are stored (once, by its first 128-row tile), bit for bit
- *        those of fp8bs_quantize_w_128x128(w); the blocks of experts without
- *        rows are not written.
+ *        both NULL.  Codes and scales are stored there once, by an expert's
+ *        first 128-row tile, bit for bit those of fp8bs_quantize_w_128x128(w):
+ *          keep_codes == 1: for every expert that owns at least one row (the
+ *            FP8 weights kept for later GEMMs, e.g. a backward's dgrad);
+ *          keep_codes == 0: only for experts with more than one 128-row tile,
+ *            whose other tiles read them back; qw / sw then serve as the
+ *            call's workspace and hold nothing defined for the other experts.
+ *        With qw == NULL nothing is stored and every tile codes its weights
+ *        from bf16 (keep_codes must be 0).  Blocks of experts without rows
+ *        are never written.
  *   qa, sa, seg_offsets, row_token, num_experts, total_rows, c: as for
  *        fp8bs_grouped_gemm, whose preconditions hold here too; n % 256 == 0.
  * c equals, bit for bit, fp8bs_grouped_gemm over the codes and scales that
- * fp8bs_quantize_w_128x128(w) gives.
+ * fp8bs_quantize_w_128x128(w) gives, in every mode.
  * Alignment: qa, w, qw, c 16-byte aligned; sa, sw, seg_offsets, row_token
- * 4-byte.  Errors: FP8BS_ERR_NULL also when exactly one of qw, sw is NULL.
+ * 4-byte.  Errors: FP8BS_ERR_NULL also when exactly one of qw, sw is NULL or
+ * when keep_codes == 1 without them; FP8BS_ERR_FLAG when keep_codes is not 0
+ * or 1.
  */
 int fp8bs_grouped_gemm_bf16w(const uint8_t* qa, const float* sa, const int32_t* seg_offsets,
                              const int32_t* row_token, int64_t num_experts, int64_t total_rows,
                              const uint16_t* w, int64_t n, int64_t k, uint16_t* c, uint8_t* qw,
-                             float* sw, void* stream);
+                             float* sw, int keep_codes, void* stream);
 
 /*
  * Weight-gradient GEMM: C[m, n] (+)= sum_t A[m, t] * B[n, t] over tokens t,

@@ -115,13 +115,15 @@ def test_grouped_validation(raw):
 
 def test_grouped_bf16w_validation(raw):
     f = raw.fp8bs_grouped_gemm_bf16w
-    assert f(P, P, P, None, 4, 512, None, 256, 128, P, None, None, None) == ENULL      # w
-    assert f(P, P, P, None, 4, 512, P, 256, 128, P, P, None, None) == ENULL           # qw without sw
-    assert f(P, P, P, None, 4, 512, P, 128, 128, P, None, None, None) == ESHAPE       # n % 256
-    assert f(P, P, P, None, 4, 500, P, 256, 128, P, None, None, None) == ESHAPE       # total_rows % 128
-    assert f(P, P, P, None, 4, 512, P, 256, 100, P, None, None, None) == ESHAPE       # k % 128
-    assert f(P, P, P, None, 4, 512, P + 2, 256, 128, P, None, None, None) == EALIGN   # w
-    assert f(P, P, P, None, 4, 512, P, 256, 128, P, P + 8, P, None) == EALIGN         # qw
+    assert f(P, P, P, None, 4, 512, None, 256, 128, P, None, None, 0, None) == ENULL      # w
+    assert f(P, P, P, None, 4, 512, P, 256, 128, P, P, None, 0, None) == ENULL           # qw without sw
+    assert f(P, P, P, None, 4, 512, P, 256, 128, P, None, None, 1, None) == ENULL        # keep without qw
+    assert f(P, P, P, None, 4, 512, P, 256, 128, P, P, P, 2, None) == EFLAG              # keep_codes
+    assert f(P, P, P, None, 4, 512, P, 128, 128, P, None, None, 0, None) == ESHAPE       # n % 256
+    assert f(P, P, P, None, 4, 500, P, 256, 128, P, None, None, 0, None) == ESHAPE       # total_rows % 128
+    assert f(P, P, P, None, 4, 512, P, 256, 100, P, None, None, 0, None) == ESHAPE       # k % 128
+    assert f(P, P, P, None, 4, 512, P + 2, 256, 128, P, None, None, 0, None) == EALIGN   # w
+    assert f(P, P, P, None, 4, 512, P, 256, 128, P, P + 8, P, 1, None) == EALIGN         # qw
 
 
 def test_wgrad_validation(raw):

@@ -685,6 +685,18 @@ def test_grouped_bf16w_equals_quantize_then_grouped(gpu_lib, k, counts):
                 f"k={k}: stored weights of expert {e}"
         else:
             assert bool((qw[e] == 0x5A).all()) and bool((sw[e] == -1.0).all()), f"k={k}: expert {e} has no rows"
+    # keep_codes=False: qw / sw as the call's workspace, holding the codes of
+    # the experts with more than one 128-row tile only
+    qw3 = torch.full_like(qw, 0x5A)
+    sw3 = torch.full_like(sw, -1.0)
+    c3 = gpu_lib.fp8bs_grouped_gemm_bf16w(qa_d, sa_d, seg, w, qw=qw3, sw=sw3, row_token=rt_d, keep_codes=False)
+    assert torch.equal(c3.view(torch.int16), c_ref.view(torch.int16)), f"k={k}: C, codes of multi-tile experts only"
+    for e in range(num_e):
+        if off[e + 1] - off[e] > 128:
+            assert torch.equal(qw3[e], qw_ref[e]) and torch.equal(sw3[e].view(torch.int32), sw_ref[e].view(torch.int32)), \
+                f"k={k}: workspace codes of expert {e}"
+        else:
+            assert bool((qw3[e] == 0x5A).all()) and bool((sw3[e] == -1.0).all()), f"k={k}: expert {e} not stored"
     for e in sorted({0, num_e - 1}):
         if not counts[e]:
             continue
@@ -694,7 +706,9 @@ def test_grouped_bf16w_equals_quantize_then_grouped(gpu_lib, k, counts):
 
 def test_grouped_bf16w_c4_full_launch(gpu_lib):
     """c4 at full size: the fused call against the two calls, whole outputs
-    bit for bit, and the stored weights of every expert with rows."""
+    bit for bit, and the stored weights of every expert with rows; then with
+    keep_codes=False: the same output, codes stored for the experts with
+    several 128-row tiles only."""
     cfg = config_by_name("c4")
     g = grouped_inputs_host(cfg, with_weights=False)
     off, counts = g["offsets"], g["counts"]
@@ -710,4 +724,13 @@ def test_grouped_bf16w_c4_full_launch(gpu_lib):
     assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16))
     has = torch.from_numpy(np.asarray(counts) > 0).cuda()
     assert torch.equal(qw[has], qw_ref[has]) and torch.equal(sw[has], sw_ref[has])
+    # the bench step's mode: codes stored only for experts with several tiles
+    multi = torch.from_numpy(np.diff(off) > 128).cuda()
+    qw.zero_()
+    sw.zero_()
+    c.zero_()
+    c = gpu_lib.fp8bs_grouped_gemm_bf16w(qa, sa, seg, w, c=c, qw=qw, sw=sw, row_token=rt_d, keep_codes=False)
+    assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16))
+    assert torch.equal(qw[multi], qw_ref[multi]) and torch.equal(sw[multi], sw_ref[multi])
+    assert not bool(qw[~multi].any()) and not bool(sw[~multi].any())
     del w, qw_ref, qw
