@@ -299,7 +299,7 @@ def build_grouped_step(lib, rotate, fused=True, keep_codes=False):
     if fused:
         calls = [
             quant_x,
-            Call("gemm_grouped_bf16w", "gemm",
+            Call("gemm_grouped_bf16w_keep_codes" if keep_codes else "gemm_grouped_bf16w", "gemm",
                  lambda: lib.fp8bs_grouped_gemm_bf16w(qx, sx, seg_pad, w, c=y, qw=qw, sw=sw, row_token=row_token,
                                                       keep_codes=keep_codes),
                  flops=2.0 * pairs * n * k, nbytes=fused_bytes, outs=(y, qw, sw) if keep_codes else (y,)),
@@ -783,6 +783,8 @@ def main():
         ent.update(call_roofline(c, avg_s))
         if c.kind == "gemm":
             ent["frac_fp8_peak"] = round(c.flops / avg_s / 1e12 / FP8_PEAK_TFLOPS, 4)
+        if ent["bound"] == "mfma":
+            ent["algorithmic_bytes"] = c.nbytes
         if copy_gbps and ent["bound"] == "hbm":
             ent["frac_copy"] = round(c.nbytes / avg_s / 1e9 / copy_gbps, 4)
         ent["traffic"] = load_traffic(f"{args.config}:{c.name}", c.kind)

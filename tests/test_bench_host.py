@@ -70,8 +70,8 @@ def test_call_roofline_picks_the_longer_bound():
     """A call's bound is whichever of its FLOPs at the dense FP8 peak and its
     algorithmic bytes at the HBM peak takes longer; `achieved` is that quantity
     per second of the measured duration."""
-    # c4's fused grouped GEMM: 1.924 TFLOP over the routed rows, 23.23 GB moved
-    flops, nbytes = 2.0 * 32768 * 4096 * 7168, 23_234_300_416
+    # c4's fused grouped GEMM: 1.924 TFLOP over the routed rows, 15.72 GB moved
+    flops, nbytes = 2.0 * 32768 * 4096 * 7168, 15_716_272_640
     c = bench.Call("gemm_grouped_bf16w", "gemm", None, flops=flops, nbytes=nbytes)
     r = bench.call_roofline(c, 5.58e-3)
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["algorithmic"] == nbytes
@@ -94,6 +94,9 @@ def test_c4_two_calls_flag_parses():
         a = bench.parse_args()
         assert a.c4_two_calls and a.config == "c4" and a.steps == 20 and a.warmup == 5
         sys.argv = ["bench.py"]
-        assert not bench.parse_args().c4_two_calls
+        a = bench.parse_args()
+        assert not a.c4_two_calls and not a.c4_keep_codes
+        sys.argv = ["bench.py", "--c4-keep-codes"]
+        assert bench.parse_args().c4_keep_codes
     finally:
         sys.argv = sys_argv
