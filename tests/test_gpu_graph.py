@@ -83,13 +83,15 @@ def test_layer_pass_graph_replays_match_eager(gpu_lib):
     assert np.isfinite(bf16_values_host(y)).all()
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_moe_forward_graph_replays_match_eager(gpu_lib, fused):
+@pytest.mark.parametrize("mode", ["two_calls", "fused", "fused_workspace"])
+def test_moe_forward_graph_replays_match_eager(gpu_lib, mode):
     """Route -> dispatch -> grouped GEMM over the row capacity -> combine, captured once.
 
     No call reads a size back to the host, so the whole MoE forward is one graph.
     The expert weights are quantized by their own call, or (fused) inside the
-    grouped GEMM from bf16 with the codes stored (two launches).  The eager
+    grouped GEMM from bf16 with the codes stored (two launches), or with codes
+    stored only for the experts whose other tiles read them back (qw/sw as the
+    call's workspace, poisoned before every replay like the outputs).  The eager
     layout is checked against the oracle; replays with poisoned outputs and
     unrelated eager work in between must reproduce the eager bits (rows past
     the padded total are not defined outputs and are left out)."""
@@ -113,8 +115,9 @@ def test_moe_forward_graph_replays_match_eager(gpu_lib, fused):
     def moe_pass():
         gpu_lib.fp8bs_moe_route(ids, 16, rows_cap=cap, seg_offsets=seg, slot_rows=slot, row_token=tok)
         gpu_lib.fp8bs_moe_permute_quantize(x, slot, seg, tok, q=q, scales=s)
-        if fused:
-            gpu_lib.fp8bs_grouped_gemm_bf16w(q, s, seg, w, c=y, qw=qw, sw=sw, row_token=tok)
+        if mode != "two_calls":
+            gpu_lib.fp8bs_grouped_gemm_bf16w(q, s, seg, w, c=y, qw=qw, sw=sw, row_token=tok,
+                                             keep_codes=mode == "fused")
         else:
             gpu_lib.fp8bs_quantize_w_128x128(w, q=qw, scales=sw)
             gpu_lib.fp8bs_grouped_gemm(q, s, seg, qw, sw, c=y, row_token=tok)
@@ -125,8 +128,11 @@ def test_moe_forward_graph_replays_match_eager(gpu_lib, fused):
     r = moe_route(d["ids"], 16)
     total = int(r["seg_offsets"][-1])
     assert np.array_equal(seg.cpu().numpy(), r["seg_offsets"]) and np.array_equal(tok.cpu().numpy(), r["row_token"])
-    # the fused call stores the weight codes of experts that have rows only
-    used = np.diff(r["seg_offsets"]) > 0 if fused else np.ones(16, bool)
+    # the fused call stores the weight codes of experts that have rows only, or
+    # (workspace) of those with more than one 128-row tile
+    rows_e = np.diff(r["seg_offsets"])
+    used = {"two_calls": np.ones(16, bool), "fused": rows_e > 0, "fused_workspace": rows_e > 128}[mode]
+    assert mode != "fused_workspace" or 0 < int(used.sum()) < 16, "the routing must mix one- and multi-tile experts"
     used_e = [int(e) for e in np.nonzero(used)[0]]
     outs = [seg, slot, tok, q[:total], s[:total], *[qw[e] for e in used_e], *[sw[e] for e in used_e],
             y[:total], out]
