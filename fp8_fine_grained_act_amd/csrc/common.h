@@ -94,19 +94,23 @@ __device__ __forceinline__ GroupScale group_scale(uint32_t amax_bits) {
 // even for a subnormal s (a few ulp above 448 otherwise), and
 // v_cvt_pk_fp8_f32 rounds every binary32 value in (448, 464] to 448 (0x7E)
 // under round-to-nearest-even (checked on gfx950 for all of them, both signs).
+//
+// The magnitudes come from the abs source modifier of the instructions that
+// first read them (no masking of the packed words), the signs from the bf16
+// sign bits; the first conversion's upper half is a placeholder (x01) that
+// the second conversion overwrites.
 template <bool SLOW>
 __device__ __forceinline__ uint32_t quant4_path(uint32_t x01, uint32_t x23, const GroupScale& g) {
-  const uint32_t m01 = x01 & 0x7FFF7FFFu, m23 = x23 & 0x7FFF7FFFu;
-  const float a[4] = {bf16_lo(m01), bf16_hi(m01), bf16_lo(m23), bf16_hi(m23)};
+  const float a[4] = {bf16_lo(x01), bf16_hi(x01), bf16_lo(x23), bf16_hi(x23)};
   float qv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float ai = SLOW ? a[i] * kTinyScale : a[i];
+    const float ai = SLOW ? __builtin_fabsf(a[i]) * kTinyScale : __builtin_fabsf(a[i]);
     const float q0 = ai * g.r;
     const float e = __builtin_fmaf(-q0, g.d, ai);
     qv[i] = __builtin_fmaf(e, g.r, q0);
   }
-  int d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+  int d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], (int)x01, false);
   d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], d, true);
   // sign bits: byte 1 and byte 3 of each bf16 pair carry them in bit 7
   const uint32_t hi_bytes = __builtin_amdgcn_perm(x23, x01, 0x07050301u);

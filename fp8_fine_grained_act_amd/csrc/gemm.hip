@@ -609,6 +609,11 @@ static int launch_gemm(GemmArgs a, hipStream_t s) {
 // dgrad), or only those of experts with several m-tiles, whose other m-tiles
 // read them back in the call's second launch.
 // ---------------------------------------------------------------------------
+// a wave-uniform float moved to a scalar register
+__device__ __forceinline__ float uniform_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 template <int BM, int BN>
 __device__ __forceinline__ void copy_waves_bf16_weights(const GemmArgs& p, int c, int lane, int units,
                                                         int64_t m0, int64_t n0, Stage<BM, BN>& st0,
@@ -672,19 +677,21 @@ __device__ __forceinline__ void copy_waves_bf16_weights(const GemmArgs& p, int c
     if (lane == 0) half_amax[kb & 1][c] = m;
   };
   // quant4_path with the tiny-tile factor as a multiplier (1 or 2^64): one
-  // code path for both (a product with 1 is exact, so the codes are the same)
+  // code path for both (a product with 1 is exact, so the codes are the same).
+  // The magnitudes come from the abs source modifier of the first multiply,
+  // the signs from the bf16 sign bits; the first conversion's upper half is a
+  // placeholder (x01) that the second overwrites.
   auto quant4 = [&](uint32_t x01, uint32_t x23, const GroupScale& gs, float mul) -> uint32_t {
-    const uint32_t m01 = x01 & 0x7FFF7FFFu, m23 = x23 & 0x7FFF7FFFu;
-    const float a[4] = {bf16_lo(m01), bf16_hi(m01), bf16_lo(m23), bf16_hi(m23)};
+    const float a[4] = {bf16_lo(x01), bf16_hi(x01), bf16_lo(x23), bf16_hi(x23)};
     float qv[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const float ai = a[t] * mul;
+      const float ai = __builtin_fabsf(a[t]) * mul;
       const float q0 = ai * gs.r;
       const float er = __builtin_fmaf(-q0, gs.d, ai);
       qv[t] = __builtin_fmaf(er, gs.r, q0);
     }
-    int d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+    int d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], (int)x01, false);
     d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], d, true);
     return (uint32_t)d | (__builtin_amdgcn_perm(x23, x01, 0x07050301u) & 0x80808080u);
   };
@@ -693,8 +700,11 @@ __device__ __forceinline__ void copy_waves_bf16_weights(const GemmArgs& p, int c
   // half of the coding, so most of their latency passes under the second)
   auto code = [&](auto load_tag, int kb, const uint4 (&b)[16], Stage<BM, BN>& s, uint4 (&next)[16], int kn) {
     constexpr bool LOAD = decltype(load_tag)::value;
-    const GroupScale gs = group_scale(max(half_amax[kb & 1][c], half_amax[kb & 1][c ^ 1]));
-    const float mul = gs.slow ? kTinyScale : 1.0f;
+    // the block's scale is the same in every lane: kept in scalar registers
+    GroupScale gs = group_scale(max(half_amax[kb & 1][c], half_amax[kb & 1][c ^ 1]));
+    gs.r = uniform_f32(gs.r);
+    gs.d = uniform_f32(gs.d);
+    const float mul = uniform_f32(gs.slow ? kTinyScale : 1.0f);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (LOAD && i < 8) {

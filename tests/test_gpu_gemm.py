@@ -649,15 +649,17 @@ def _routed_rows(counts):
 
 
 @pytest.mark.parametrize("k,counts", [(128, [130, 0, 1, 256, 77]), (256, [130, 0, 1, 256, 77]),
-                                      (384, [130, 0, 1, 256, 77]), (640, [130, 0, 1, 256, 77]),
-                                      (896, [130, 0, 1, 256, 77]), (384, [0, 5, 0, 300, 0]), (256, [200])])
+                                      (384, [130, 0, 1, 256, 77]), (512, [130, 0, 1, 256, 77]),
+                                      (640, [130, 0, 1, 256, 77]), (768, [130, 0, 1, 256, 77]),
+                                      (896, [130, 0, 1, 256, 77]), (384, [0, 5, 0, 300, 0]), (256, [200]),
+                                      (1280, [300, 129])])
 def test_grouped_bf16w_equals_quantize_then_grouped(gpu_lib, k, counts):
     """The fused call (weights coded in the GEMM's copy waves) against
     fp8bs_quantize_w_128x128 followed by fp8bs_grouped_gemm: C bit for bit,
     with and without the row map; the stored codes and scales equal the block
     quantizer's for every expert with rows and leave an expert without rows
-    untouched.  K = 128 .. 896 runs 1, 2, 3, 5 and 7 slab units (the copy
-    waves alternate two register buffers); the routings include empty first
+    untouched.  K = 128 .. 1280 runs 1 to 7 and 10 slab units (the copy waves
+    alternate two register buffers); the routings include empty first
     and last experts and a single expert.  The first and last experts' stored
     blocks (zero, tiny and large ones) are also checked against the oracle."""
     rng = np.random.default_rng(240 + k + len(counts))
