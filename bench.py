@@ -5,7 +5,7 @@ Default workload (``--config c4``, the largest configuration): the MoE routed-
 expert grouped GEMM of 4096 tokens x top-8 of 256 experts (Zipf 1.1 counts,
 each expert's rows padded to a multiple of 128), fused gate+up N = 4096,
 K = 7168.  One step runs the configuration's whole FP8 path:
-    quantize X (1x128 tiles, the padded expert-major rows)
+    quantize X (1x128 tiles, the routed rows of the padded expert-major layout)
     quantize every expert's W (128x128 blocks, 256 x 4096 x 7168)
     grouped GEMM C = X W_e^T per expert segment (bf16 out)
 ``value`` = the grouped GEMM's FLOPs over the routed (real) rows,
@@ -240,8 +240,9 @@ def build_layer_step(lib, cfg_name, rotate, dual=True, act_cache=False):
 def build_grouped_step(lib, rotate, fused=True, keep_codes=False):
     """Calls of configuration c4: the MoE expert grouped GEMM with its quantization.
 
-    The step: quantize X (1x128 tiles over the padded expert-major rows; the
-    padding rows are +0.0) -> quantize every expert's weight (128x128 blocks,
+    The step: quantize X (1x128 tiles over the routed rows of the padded
+    expert-major layout; the padding rows, which the grouped GEMM does not read
+    through the row map, are not coded) -> quantize every expert's weight (128x128 blocks,
     codes and scales stored) -> grouped GEMM over the padded total.  By
     default the last two are one call, fp8bs_grouped_gemm_bf16w, whose copy
     waves code each weight block where the GEMM reads it; it stores the codes
@@ -281,10 +282,10 @@ def build_grouped_step(lib, rotate, fused=True, keep_codes=False):
     y = e(total, n, dt=bf16)
     state = {"i": 0}
     kb = k // 128
-    # algorithmic bytes: the X quantizer reads and writes every padded row; the
+    # algorithmic bytes: the X quantizer reads and writes the routed rows and reads the row map; the
     # grouped GEMM reads the routed rows of X (the row map clips the padding),
     # the row map, every expert weight once, and writes every padded output row
-    x_bytes = total * k * 3 + total * kb * 4
+    x_bytes = pairs * (k * 3 + kb * 4) + total * 4
     w_bytes = num_e * n * k * 3 + num_e * (n // 128) * kb * 4
     gemm_bytes = pairs * (k + kb * 4) + total * 4 + num_e * (n * k + (n // 128) * kb * 4) + total * n * 2
     # fused: the bf16 weights read once, the routed rows of X and the row map
@@ -294,7 +295,9 @@ def build_grouped_step(lib, rotate, fused=True, keep_codes=False):
     # workspace and are not counted.
     fused_bytes = (num_e * n * k * 2 + pairs * (k + kb * 4) + total * 4 + total * n * 2
                    + (num_e * n * k + num_e * (n // 128) * kb * 4 if keep_codes else 0))
-    quant_x = Call("quant_act_x", "quant", lambda: lib.fp8bs_quantize_act_1x128(x, q=qx, scales=sx),
+    # X: only the routed rows are coded (the grouped GEMM reads no padding row through the row map)
+    quant_x = Call("quant_act_x", "quant",
+                   lambda: lib.fp8bs_quantize_act_1x128_routed(x, row_token, q=qx, scales=sx),
                    nbytes=x_bytes, outs=(qx, sx))
     if fused:
         calls = [
@@ -339,19 +342,20 @@ def build_grouped_step(lib, rotate, fused=True, keep_codes=False):
              nbytes=pairs * k * 2 + tokens * topk * 8 + tokens * k * 2, outs=(out,)),
     ]
     if not fused:
-        step = "1x128 quantization of the padded rows + 128x128 quantization of all 256 expert weights + grouped GEMM"
+        step = "1x128 quantization of the routed rows + 128x128 quantization of all 256 expert weights + grouped GEMM"
     elif keep_codes:
-        step = ("1x128 quantization of the padded rows + grouped GEMM from the bf16 expert weights, each 128x128 "
+        step = ("1x128 quantization of the routed rows + grouped GEMM from the bf16 expert weights, each 128x128 "
                 "weight block quantized in the GEMM and its codes and scales stored once per expert")
     else:
-        step = ("1x128 quantization of the padded rows + grouped GEMM from the bf16 expert weights, each 128x128 "
+        step = ("1x128 quantization of the routed rows + grouped GEMM from the bf16 expert weights, each 128x128 "
                 "weight block quantized in the GEMM (codes stored once only for the experts with several "
                 "128-row tiles, which read them back)")
     desc = dict(workload="c4: MoE expert grouped GEMM, 4096 tokens x top-8 of 256 experts (Zipf 1.1 counts, "
                          "rows padded to 128 per expert), fused gate+up N=4096, K=7168; step = " + step,
                 routed_rows=pairs, padded_rows=total, experts=num_e, N=n, K=k,
                 value_flops="grouped GEMM over the routed rows, 2*32768*4096*7168",
-                bytes_counted="X quantizer: padded rows; grouped GEMM: routed rows of X, padded output rows"
+                bytes_counted="X quantizer: routed rows and the row map; grouped GEMM: routed rows of X, "
+                              "padded output rows"
                               + (("; bf16 weights read once" + (", codes written once" if keep_codes else ""))
                                  if fused else ""))
     data = dict(kind="c4", x=host["x"], counts=counts, offsets=offsets, w_dev=w, cfg=cfg)
@@ -565,8 +569,8 @@ def _oracle_sample_grouped(data, rows=512):
     Every expert's weight has the same shape, so one expert's 128x128
     quantization stands for each of the 256; the 1x128 quantization and the
     GEMM cost in proportion to their rows, so ``rows`` routed rows of the
-    largest expert (a GEMM of realistic height) stand for the padded rows
-    (quantization) and the routed rows (GEMM).  Returns the sample and a
+    largest expert (a GEMM of realistic height) stand for the routed rows
+    (quantization and GEMM).  Returns the sample and a
     function that turns the sample's time into the whole step's time.
     """
     import numpy as np
@@ -576,7 +580,7 @@ def _oracle_sample_grouped(data, rows=512):
 
     counts, off, x = data["counts"], data["offsets"], data["x"]
     n, k = data["cfg"]["N"], data["cfg"]["K"]
-    num_e, routed, padded = len(counts), int(counts.sum()), int(off[-1])
+    num_e, routed = len(counts), int(counts.sum())
     e0 = int(np.argmax(counts))
     rows = min(rows, int(counts[e0]))
     xs = x[off[e0]:off[e0] + rows]
@@ -597,12 +601,11 @@ def _oracle_sample_grouped(data, rows=512):
         parts["gemm"] += t3 - t2
 
     def step_seconds(reps):
-        return (num_e * parts["w"] + padded / rows * parts["x"] + routed / rows * parts["gemm"]) / reps
+        return (num_e * parts["w"] + routed / rows * (parts["x"] + parts["gemm"])) / reps
 
     text = (f"128x128 quantization of expert #{e0}'s weight [{n},{k}] (x{num_e} experts), 1x128 quantization of "
-            f"{rows} of its routed rows (x{padded / rows:.1f} for the {padded} padded rows) and their GEMM "
-            f"(x{routed / rows:.1f} for the {routed} routed rows); value = the step's routed-row GEMM FLOPs / "
-            f"the step time so scaled")
+            f"{rows} of its routed rows and their GEMM (both x{routed / rows:.1f} for the {routed} routed rows); "
+            f"value = the step's routed-row GEMM FLOPs / the step time so scaled")
     return one, 2.0 * routed * n * k, text, step_seconds
 
 

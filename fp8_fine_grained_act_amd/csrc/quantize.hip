@@ -17,20 +17,28 @@ namespace fp8bs {
 // 1x128 tiles along the columns: x [rows, cols] -> q [rows, cols], s [rows, cols/128]
 // One tile = 128 bf16 = 256 bytes, handled by 8 lanes (16 elements = 32 bytes each).
 // A 256-thread block covers 32 consecutive tiles (row-major tile order).
+// ROUTED: only the rows whose row_token entry is >= 0 are read and written
+// (the rows that carry a routed token in an expert-major padded layout); the
+// 8 lanes of a tile share its row, so a skipped tile's lanes reduce zeros.
 // ---------------------------------------------------------------------------
+template <bool ROUTED>
 __global__ __launch_bounds__(256) void quant_act_rows_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-    float* __restrict__ scales, int64_t tiles_per_row, int64_t total_tiles) {
+    float* __restrict__ scales, int64_t tiles_per_row, int64_t total_tiles,
+    const int32_t* __restrict__ row_token) {
   const int lane8 = threadIdx.x & 7;
   const int64_t tile = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
-  const bool valid = tile < total_tiles;
-  const int64_t t = valid ? tile : total_tiles - 1;   // keep the reduction converged
+  const int64_t t = tile < total_tiles ? tile : total_tiles - 1;   // keep the reduction converged
   const int64_t row = t / tiles_per_row;
   const int64_t tb = t - row * tiles_per_row;
+  const bool valid = tile < total_tiles && (!ROUTED || row_token[row] >= 0);
 
   const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx + tb * kGroup + lane8 * 16);
-  uint4 v0 = src[0];
-  uint4 v1 = src[1];
+  uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+  if (!ROUTED || valid) {
+    v0 = src[0];
+    v1 = src[1];
+  }
 
   constexpr uint32_t kMag = 0x7FFF7FFFu;
   const uint32_t m2 = max_u16x2(max_u16x2(max_u16x2(v0.x & kMag, v0.y & kMag), max_u16x2(v0.z & kMag, v0.w & kMag)),
@@ -265,8 +273,8 @@ extern "C" int fp8bs_quantize_act_1x128(const uint16_t* x, int64_t rows, int64_t
     const int64_t total = rows * tpr;
     const int64_t blocks = (total + 31) / 32;
     if (blocks > kMaxGrid) return FP8BS_ERR_SHAPE;
-    hipLaunchKernelGGL(quant_act_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, ldx, q,
-                       ldq, scales, tpr, total);
+    hipLaunchKernelGGL(quant_act_rows_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, x, ldx, q,
+                       ldq, scales, tpr, total, (const int32_t*)nullptr);
   } else {
     if (rows % kGroup || cols % 8 || ldq < rows) return FP8BS_ERR_SHAPE;
     if (!cols_grid_ok(rows, cols)) return FP8BS_ERR_SHAPE;
@@ -277,6 +285,23 @@ extern "C" int fp8bs_quantize_act_1x128(const uint16_t* x, int64_t rows, int64_t
       hipLaunchKernelGGL((quant_act_cols_kernel<false, false>), cols_grid(rows, cols), dim3(256), 0, s, x,
                          ldx, rows, cols, q, ldq, scales, (uint8_t*)nullptr, (int64_t)0, (float*)nullptr);
   }
+  return launch_status();
+}
+
+extern "C" int fp8bs_quantize_act_1x128_routed(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                               const int32_t* row_token, uint8_t* q, int64_t ldq,
+                                               float* scales, void* stream) {
+  if (!x || !row_token || !q || !scales) return FP8BS_ERR_NULL;
+  if (rows <= 0 || cols <= 0 || cols % kGroup || ldx < cols || ldq < cols) return FP8BS_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4) || !aligned(row_token, 4) || ldx % 8 ||
+      ldq % 16)
+    return FP8BS_ERR_ALIGN;
+  const int64_t tpr = cols / kGroup;
+  const int64_t total = rows * tpr;
+  const int64_t blocks = (total + 31) / 32;
+  if (blocks > kMaxGrid) return FP8BS_ERR_SHAPE;
+  hipLaunchKernelGGL(quant_act_rows_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x,
+                     ldx, q, ldq, scales, tpr, total, row_token);
   return launch_status();
 }
 

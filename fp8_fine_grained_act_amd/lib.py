@@ -22,6 +22,8 @@ _c_void_p, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 
 _SIGNATURES = {
     "fp8bs_quantize_act_1x128": [_c_void_p, _i64, _i64, _i64, _int, _c_void_p, _i64, _c_void_p, _c_void_p],
+    "fp8bs_quantize_act_1x128_routed": [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _i64, _c_void_p,
+                                        _c_void_p],
     "fp8bs_quantize_act_1x128_dual": [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _i64,
                                       _c_void_p, _c_void_p],
     "fp8bs_quantize_w_128x128": [_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p],
@@ -125,6 +127,31 @@ def fp8bs_quantize_act_1x128(x, transpose=0, q=None, scales=None, stream=None):
     st = raw.fp8bs_quantize_act_1x128(x.data_ptr(), rows, cols, ldx, int(bool(transpose)), q.data_ptr(), ldq,
                                       scales.data_ptr(), _stream(stream))
     _check("fp8bs_quantize_act_1x128", st)
+    return q, scales
+
+
+def fp8bs_quantize_act_1x128_routed(x, row_token, q=None, scales=None, stream=None):
+    """1x128 tiles along the columns of the rows of bf16 x [rows, cols] whose
+    row_token entry (int32 [rows]) is >= 0; the other rows of q and scales are
+    left as they are.  Returns (q [rows, cols], scales [rows, cols/128])."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(row_token, torch.int32, "row_token")
+    ldx = _row_major(x, "x")
+    rows, cols = x.shape
+    if tuple(row_token.shape) != (rows,) or not row_token.is_contiguous():
+        raise ValueError("row_token must be a contiguous int32 [rows]")
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // GROUP), dtype=torch.float32, device=x.device)
+    _dev(q, torch.uint8, "q")
+    _dev(scales, torch.float32, "scales")
+    ldq = _row_major(q, "q")
+    if tuple(q.shape) != (rows, cols) or tuple(scales.shape) != (rows, cols // GROUP) or not scales.is_contiguous():
+        raise ValueError("output shapes do not match the input")
+    st = raw.fp8bs_quantize_act_1x128_routed(x.data_ptr(), rows, cols, ldx, row_token.data_ptr(), q.data_ptr(), ldq,
+                                             scales.data_ptr(), _stream(stream))
+    _check("fp8bs_quantize_act_1x128_routed", st)
     return q, scales
 
 

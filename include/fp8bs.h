@@ -98,6 +98,32 @@ int fp8bs_quantize_act_1x128(const uint16_t* x, int64_t rows, int64_t cols, int6
                              void* stream);
 
 /*
+ * 1x128 tiles along the columns of the routed rows of an expert-major
+ * padded activation only.  The routed experts take each token's row into
+ * 128-row segments whose padding rows carry no token (deepseek.csdn.net
+ * page, section 一(二) "DeepSeekMoE 架构": 256 routed experts, 8 per token);
+ * the expert GEMM reads only the routed rows of its FP8 input when it is
+ * given the same row map (fp8bs_grouped_gemm and fp8bs_grouped_gemm_bf16w,
+ * argument row_token), so the padding rows need no codes.  Each routed row
+ * is coded exactly as by fp8bs_quantize_act_1x128 with transpose == 0
+ * ("DeepSeek-V3 技术报告深度解读", section 3: one scale per 1x128 tile).
+ *   x          bf16 [rows, cols], row stride ldx elements (device)
+ *   row_token  int32 [rows] (device): row r is coded when row_token[r] >= 0
+ *              (the token of the row, as fp8bs_moe_route writes it) and left
+ *              alone, not read and not written, when it is negative
+ *   q          E4M3 [rows, cols], row stride ldq bytes
+ *   scales     f32 [rows, cols/128], contiguous
+ *   cols % 128 == 0.
+ * Errors: FP8BS_ERR_NULL for a null pointer, FP8BS_ERR_SHAPE, FP8BS_ERR_ALIGN
+ * (x and q 16 bytes, ldx % 8 == 0, ldq % 16 == 0, scales and row_token
+ * 4 bytes), FP8BS_ERR_LAUNCH.  The outputs of skipped rows keep their
+ * previous contents.
+ */
+int fp8bs_quantize_act_1x128_routed(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                    const int32_t* row_token, uint8_t* q, int64_t ldq, float* scales,
+                                    void* stream);
+
+/*
  * Both orientations of the 1x128 activation tiles from one read of x.
  * In a training step an activation (and its output gradient) is the FP8
  * input of two GEMMs with different contractions ("DeepSeek-V3 技术报告深度解读",

@@ -68,6 +68,19 @@ def test_quantize_act_validation(raw):
     assert f(P, 128, 64, 64, 1, P, 64, P, None) == ESHAPE           # transposed: ldq < rows
 
 
+def test_quantize_act_routed_validation(raw):
+    f = raw.fp8bs_quantize_act_1x128_routed
+    assert f(P, 4, 128, 128, None, P, 128, P, None) == ENULL         # row map required
+    assert f(None, 4, 128, 128, P, P, 128, P, None) == ENULL
+    assert f(P, 4, 100, 128, P, P, 128, P, None) == ESHAPE           # cols % 128
+    assert f(P, 0, 128, 128, P, P, 128, P, None) == ESHAPE
+    assert f(P, 4, 128, 64, P, P, 128, P, None) == ESHAPE            # ldx < cols
+    assert f(P, 4, 128, 128, P, P, 64, P, None) == ESHAPE            # ldq < cols
+    assert f(P_ODD, 4, 128, 128, P, P, 128, P, None) == EALIGN
+    assert f(P, 4, 128, 128, P + 2, P, 128, P, None) == EALIGN       # row map 4-byte aligned
+    assert f(P, 4, 128, 130, P, P, 128, P, None) == EALIGN           # ldx % 8
+
+
 def test_quantize_act_dual_validation(raw):
     f = raw.fp8bs_quantize_act_1x128_dual
     assert f(P, 128, 128, 128, P, 128, P, None, 128, P, None) == ENULL

@@ -140,6 +140,44 @@ def test_act_rows_moe_padded_input(gpu_lib):
     assert np.all(q[pad] == 0) and np.all(s[pad] == 0)
 
 
+def test_act_routed_rows_small_and_edges(gpu_lib):
+    """Only the rows with a row-map entry >= 0 are coded, bit-exactly as the
+    plain call codes them (edge rows included); the other rows keep what the
+    output buffers held."""
+    rng = np.random.default_rng(77)
+    bits = _edge_matrix(rng, 37, 384)
+    rt = np.where(rng.random(37) < 0.6, np.arange(37), -1).astype(np.int32)
+    rt[:7] = np.arange(7)                                         # every edge row is coded
+    rt[-1] = -1
+    q = torch.full((37, 384), 0x5A, dtype=torch.uint8, device="cuda")
+    s = torch.full((37, 3), -2.0, dtype=torch.float32, device="cuda")
+    gpu_lib.fp8bs_quantize_act_1x128_routed(to_dev_bf16(bits), torch.from_numpy(rt).cuda(), q=q, scales=s)
+    torch.cuda.synchronize()
+    qh, sh = q.cpu().numpy(), s.cpu().numpy()
+    live = rt >= 0
+    _assert_same("routed rows", qh[live], sh[live], *quantize_act_1x128(bits[live]))
+    assert np.all(qh[~live] == 0x5A) and np.all(sh[~live] == -2.0)
+
+
+def test_act_routed_rows_c4(gpu_lib):
+    """c4's padded expert-major X with the routing's row map: the routed rows
+    equal the plain call's codes and scales, the padding rows are untouched."""
+    cfg = config_by_name("c4")
+    g = grouped_inputs_host(cfg, with_weights=False)
+    bits, off, counts = g["x"], g["offsets"], g["counts"]
+    rt = np.full(bits.shape[0], -1, np.int32)
+    for e, cnt in enumerate(counts):
+        rt[off[e]:off[e] + cnt] = np.arange(cnt, dtype=np.int32)
+    x = to_dev_bf16(bits)
+    q_ref, s_ref = gpu_lib.fp8bs_quantize_act_1x128(x)
+    q = torch.full_like(q_ref, 0xA5)
+    s = torch.full_like(s_ref, 3.0)
+    gpu_lib.fp8bs_quantize_act_1x128_routed(x, torch.from_numpy(rt).cuda(), q=q, scales=s)
+    live = torch.from_numpy(rt >= 0).cuda()
+    assert torch.equal(q[live], q_ref[live]) and torch.equal(s[live].view(torch.int32), s_ref[live].view(torch.int32))
+    assert bool((q[~live] == 0xA5).all()) and bool((s[~live] == 3.0).all())
+
+
 def test_act_transposed_small_and_ragged(gpu_lib):
     rng = np.random.default_rng(103)
     for t, c in [(128, 8), (128, 72), (256, 200), (384, 64), (1024, 520)]:
