@@ -19,7 +19,7 @@ namespace fp8bs {
 // A 256-thread block covers 32 consecutive tiles (row-major tile order).
 // ROUTED: only the rows whose row_token entry is >= 0 are read and written
 // (the rows that carry a routed token in an expert-major padded layout); the
-// 8 lanes of a tile share its row, so a skipped tile's lanes reduce zeros.
+// 8 lanes of a tile share its row, and a skipped tile's lanes return at once.
 // ---------------------------------------------------------------------------
 template <bool ROUTED>
 __global__ __launch_bounds__(256) void quant_act_rows_kernel(
@@ -32,13 +32,13 @@ __global__ __launch_bounds__(256) void quant_act_rows_kernel(
   const int64_t row = t / tiles_per_row;
   const int64_t tb = t - row * tiles_per_row;
   const bool valid = tile < total_tiles && (!ROUTED || row_token[row] >= 0);
+  // a skipped tile's 8 lanes leave together; the amax exchange below never
+  // reads a lane outside its own tile's 8
+  if (ROUTED && !valid) return;
 
   const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx + tb * kGroup + lane8 * 16);
-  uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-  if (!ROUTED || valid) {
-    v0 = src[0];
-    v1 = src[1];
-  }
+  uint4 v0 = src[0];
+  uint4 v1 = src[1];
 
   constexpr uint32_t kMag = 0x7FFF7FFFu;
   const uint32_t m2 = max_u16x2(max_u16x2(max_u16x2(v0.x & kMag, v0.y & kMag), max_u16x2(v0.z & kMag, v0.w & kMag)),
