@@ -157,6 +157,16 @@ def test_act_routed_rows_small_and_edges(gpu_lib):
     live = rt >= 0
     _assert_same("routed rows", qh[live], sh[live], *quantize_act_1x128(bits[live]))
     assert np.all(qh[~live] == 0x5A) and np.all(sh[~live] == -2.0)
+    # strided input and codes (ldx = 512, ldq = 416): the same bits, the gaps untouched
+    xw = torch.zeros((37, 512), dtype=torch.bfloat16, device="cuda")
+    xw[:, :384] = to_dev_bf16(bits)
+    qw_ = torch.full((37, 416), 0x33, dtype=torch.uint8, device="cuda")
+    s2 = torch.full((37, 3), -2.0, dtype=torch.float32, device="cuda")
+    gpu_lib.fp8bs_quantize_act_1x128_routed(xw[:, :384], torch.from_numpy(rt).cuda(), q=qw_[:, :384], scales=s2)
+    torch.cuda.synchronize()
+    q2 = qw_.cpu().numpy()
+    assert np.array_equal(q2[live, :384], qh[live]) and np.array_equal(s2.cpu().numpy(), sh)
+    assert np.all(q2[~live] == 0x33) and np.all(q2[:, 384:] == 0x33)
 
 
 def test_act_routed_rows_c4(gpu_lib):
