@@ -15,15 +15,19 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 constexpr int kGroup = 128;           // scale-group length along the contraction
 constexpr float kE4M3Max = 448.0f;
 
-// x / s is evaluated as q0 = x*r, e = fma(-q0, s, x), q = fma(e, r, q0) with
-// r = 1/s correctly rounded (Markstein's correction step).  An exhaustive
-// host check over every pair of bf16 values (amax, |x| <= amax) shows that
-// this gives the same E4M3 code as the IEEE quotient whenever amax >= 2^-104.
-// Tiles whose amax (bf16 bits, sign cleared) is below kTinyAmaxBits (2^-64,
-// far inside that range) run the same step on x * 2^64 and s * 2^64: both
-// products are exact (s may be subnormal, s * 2^64 is normal), the quotient
-// is unchanged, and 1 / (s * 2^64) is finite; the same host check covers
-// every pair of that range.  A zero tile has s = r = 0, which yields q = 0.
+// x / s is evaluated as q = fma(x, r, x * rl) with r = 1/s correctly rounded
+// and rl = fl32(fma(-s, r, 1) * r) its low part: 1 - s*r is exact in binary32
+// for the correctly rounded reciprocal, so r + rl carries 1/s to about 2^-48
+// relative, and the fma rounds x*(r + rl) once.  That is not a correctly
+// rounded quotient for every binary32 x, but x here is a bf16 value: an
+// exhaustive host check over every pair of bf16 values (amax, |x| <= amax)
+// shows that it gives the same E4M3 code as the IEEE quotient, and never
+// exceeds 464.  Tiles whose amax (bf16 bits, sign cleared) is below
+// kTinyAmaxBits (2^-64) run the same two operations on x * 2^64 and
+// s * 2^64: both products are exact (s may be subnormal, s * 2^64 is normal),
+// the quotient is unchanged, and 1 / (s * 2^64) is finite; the same host
+// check covers every pair of that range.  A zero tile has s = r = rl = 0,
+// which yields q = 0.
 constexpr uint32_t kTinyAmaxBits = 0x1F80u;
 
 // ---- cross-lane max inside a row of 16 lanes (DPP, no LDS traffic) ----------
@@ -72,8 +76,9 @@ constexpr float kTinyScale = 0x1p64f;
 // Per-group quantization constants derived from the group's amax (bf16 bits).
 struct GroupScale {
   float s;     // dequantization scale amax / 448 (IEEE division), the stored scale
-  float d;     // divisor of the correction step: s, or s * 2^64 for a tiny tile
+  float d;     // divisor: s, or s * 2^64 for a tiny tile
   float r;     // 1 / d correctly rounded (0 for an all-zero tile)
+  float rl;    // low part of 1 / d: fl32(fma(-d, r, 1) * r) (0 for an all-zero tile)
   bool slow;   // tiny tile: the values are multiplied by 2^64 first
 };
 
@@ -84,6 +89,7 @@ __device__ __forceinline__ GroupScale group_scale(uint32_t amax_bits) {
   g.slow = amax_bits < kTinyAmaxBits;
   g.d = g.slow ? g.s * kTinyScale : g.s;
   g.r = g.d == 0.0f ? 0.0f : 1.0f / g.d;
+  g.rl = __builtin_fmaf(-g.d, g.r, 1.0f) * g.r;
   return g;
 }
 
@@ -106,9 +112,7 @@ __device__ __forceinline__ uint32_t quant4_path(uint32_t x01, uint32_t x23, cons
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float ai = SLOW ? __builtin_fabsf(a[i]) * kTinyScale : __builtin_fabsf(a[i]);
-    const float q0 = ai * g.r;
-    const float e = __builtin_fmaf(-q0, g.d, ai);
-    qv[i] = __builtin_fmaf(e, g.r, q0);
+    qv[i] = __builtin_fmaf(ai, g.r, ai * g.rl);
   }
   int d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], (int)x01, false);
   d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], d, true);

@@ -687,9 +687,7 @@ __device__ __forceinline__ void copy_waves_bf16_weights(const GemmArgs& p, int c
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float ai = __builtin_fabsf(a[t]) * mul;
-      const float q0 = ai * gs.r;
-      const float er = __builtin_fmaf(-q0, gs.d, ai);
-      qv[t] = __builtin_fmaf(er, gs.r, q0);
+      qv[t] = __builtin_fmaf(ai, gs.r, ai * gs.rl);
     }
     int d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], (int)x01, false);
     d = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], d, true);
@@ -703,7 +701,7 @@ __device__ __forceinline__ void copy_waves_bf16_weights(const GemmArgs& p, int c
     // the block's scale is the same in every lane: kept in scalar registers
     GroupScale gs = group_scale(max(half_amax[kb & 1][c], half_amax[kb & 1][c ^ 1]));
     gs.r = uniform_f32(gs.r);
-    gs.d = uniform_f32(gs.d);
+    gs.rl = uniform_f32(gs.rl);
     const float mul = uniform_f32(gs.slow ? kTinyScale : 1.0f);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {

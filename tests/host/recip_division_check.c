@@ -5,8 +5,8 @@
  *   amax >= threshold (2^-64 in the kernels): d = s, r = fl32(1/d), a = x;
  *   amax <  threshold (tiny tiles):           d = s * 2^64, r = fl32(1/d)
  *                                             (0 when d == 0), a = x * 2^64;
- * the correction step
- *     q0 = a*r;  e = fma(-q0, d, a);  q = fma(e, r, q0)
+ * with rl = fl32(fma(-d, r, 1) * r), the low part of 1/d, the quotient
+ *     q = fma(a, r, fl32(a * rl))
  * must give the same E4M3 code (round to nearest even, saturating) as the
  * IEEE binary32 quotient x/s, and q must not exceed 464 (the hardware
  * conversion rounds (448, 464] to 448; above that it would not saturate).
@@ -46,12 +46,12 @@ static long long check_range(uint32_t lo, uint32_t hi, int tiny, long long* pair
     float s = amax / 448.0f;
     float d = tiny ? s * 0x1p64f : s;
     float r = d == 0.0f ? 0.0f : 1.0f / d;
+    float rl = fmaf(-d, r, 1.0f) * r;
     for (uint32_t xb = 0; xb <= ab; ++xb) {
       float x = from_bf16(xb);
       float a = tiny ? x * 0x1p64f : x;
-      float q0 = a * r;
-      float e = fmaf(-q0, d, a);
-      float q = fmaf(e, r, q0);
+      float t = a * rl;
+      float q = fmaf(a, r, t);
       float ref = s == 0.0f ? 0.0f : x / s;
       ++*pairs;
       if (e4m3(q) != e4m3(ref) || q > 464.0f) {

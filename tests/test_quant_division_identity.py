@@ -1,6 +1,7 @@
-"""The HIP quantizers evaluate x / s with a per-tile reciprocal and one FMA
-correction step instead of a full division per element (tiles with a tiny
-amax run the same step on values and divisor scaled by 2^64).  This CPU test
+"""The HIP quantizers evaluate x / s with a per-tile reciprocal split in two
+parts, r = fl32(1/s) and rl = fl32(fma(-s, r, 1) * r), and one FMA per element,
+q = fma(x, r, x * rl), instead of a full division (tiles with a tiny amax run
+the same two operations on values and divisor scaled by 2^64).  This CPU test
 proves that both forms give the E4M3 code of the IEEE quotient for every pair
 of bf16 inputs (all amax, every |x| <= amax), by exhaustive enumeration in C
 (gcc, IEEE fmaf)."""
